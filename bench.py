@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of exact split-KV attention + merge on one MI355X.
+
+One step = one fused ``splitkv_attn`` call (partial attention of every LPT unit,
+then the log-sum-exp merge) over the whole workload, inputs resident in HBM.
+Prints one JSON line. Default workload: 8 sequences with contexts in [4096, 32768],
+16 trailing causal queries, GQA 32/8, head_dim 128, KV block 512, 256 workers (bf16).
+
+    python bench.py [--steps K] [--warmup W] [--workload batch8|long|lognormal|mixed|decode|small]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "split-KV attention+merge effective HBM GB/s & TFLOP/s, % of MI355X roofline"
+
+
+def _kernel_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("partial_bf16.hip", "partial_f32.hip", "merge.hip", "abi.cpp", "plan.cpp", "kernels.hpp",
+              "plan_image.hpp"):
+        with open(os.path.join(ROOT, "split_kv_exact_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(wl_key: str):
+    """HBM bytes per partial-attention launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel sources; otherwise None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{wl_key}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_sha") != _kernel_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def _time_loop(fn, steps, stream, flush=None):
+    """Mean milliseconds per call of fn over ``steps`` calls, timed with HIP events on
+    the stream the library launches on. With ``flush``, each call is preceded (outside
+    the events) by a write of a 1 GiB buffer that evicts L2 and the 256 MiB MALL."""
+    import torch
+
+    if flush is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / steps
+    tot = 0.0
+    for _ in range(steps):
+        flush.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        tot += e0.elapsed_time(e1)
+    return tot / steps
+
+
+def cpu_baseline(wl, q, k, v, budget_s: float):
+    """Time the oracle (float64, NumPy) on the host over (sequence, KV head) groups of
+    the same workload, in order, until ``budget_s`` seconds of oracle work or the whole
+    workload is done. Widening the device data to float64 is not timed."""
+    import numpy as np
+
+    from oracle import attend_rows
+    from split_kv_exact_amd.metrics import visible_pairs  # noqa: F401
+    from workloads import widen_to_f64
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    qo = np.concatenate([[0], np.cumsum(wl.q_lens)]).astype(np.int64)
+    ko = np.concatenate([[0], np.cumsum(wl.kv_lens)]).astype(np.int64)
+    g, d, es = wl.group, wl.head_dim, wl.elem_bytes
+    sc = 1.0 / math.sqrt(d)
+    spent, done_bytes, done_flops, groups = 0.0, 0, 0, 0
+    total_groups = wl.batch * wl.num_kv_heads
+    for s in range(wl.batch):
+        n, qs = wl.kv_lens[s], wl.q_lens[s]
+        for kap in range(wl.num_kv_heads):
+            Qr = widen_to_f64(q[qo[s]:qo[s + 1], kap * g:(kap + 1) * g]).reshape(qs * g, d)
+            Kh = widen_to_f64(k[ko[s]:ko[s + 1], kap])
+            Vh = widen_to_f64(v[ko[s]:ko[s + 1], kap])
+            pos = np.repeat(np.arange(n - qs, n, dtype=np.int64), g)
+            t0 = time.perf_counter()
+            attend_rows(Qr, pos, Kh, Vh, sc, wl.causal)
+            spent += time.perf_counter() - t0
+            groups += 1
+            done_bytes += qs * g * d * es + 2 * n * d * es + qs * g * (d + 1) * 4
+            pairs = qs * n - qs * (qs - 1) // 2 if wl.causal else qs * n
+            done_flops += 4 * d * g * pairs
+            if spent >= budget_s:
+                break
+        if spent >= budget_s:
+            break
+    return {
+        "value": round(done_bytes / spent / 1e9, 4),
+        "unit": "GB/s",
+        "tflops": round(done_flops / spent / 1e12, 6),
+        "cores": int(threads),
+        "kind": "oracle",
+        "seconds": round(spent, 3),
+        "sample": f"{groups} of {total_groups} (sequence, KV head) groups of the same workload, in order, "
+                  f"float64 NumPy oracle (two-pass softmax by definition); effective bytes Q+K+V+O+LSE of "
+                  f"the processed groups / oracle time",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="batch8")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cold-cache per-step measurement")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: split-KV here runs on the 256 CUs of a single MI355X; "
+              "multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import split_kv_exact_amd as skv
+    from split_kv_exact_amd import metrics as M
+    from workloads import get_workload, make_qkv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = get_workload(args.workload)
+    print(f"[bench] workload {wl.name}: drawing inputs", file=sys.stderr, flush=True)
+    q, k, v = make_qkv(wl, dev)
+
+    # Planner (host) timing: median of repeated calls.
+    plan_times = []
+    for _ in range(20):
+        t0 = time.perf_counter_ns()
+        plan = skv.plan_for(wl)
+        plan_times.append((time.perf_counter_ns() - t0) / 1e6)
+    plan_times.sort()
+    info = plan.info()
+    dev_plan = skv.splitkv_plan_upload(plan, dev)
+    ws = skv.workspace(plan, dev)
+    out = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((wl.total_q, wl.num_q_heads), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        skv.splitkv_attn(plan, dev_plan, q, k, v, ws, out, lse)
+
+    def partial():
+        skv.splitkv_partial_attn(plan, dev_plan, q, k, v, ws)
+
+    def merge():
+        skv.splitkv_merge(plan, dev_plan, ws, out, lse)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K fused steps, synchronised on both sides.
+    print("[bench] timed steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ms_step = _time_loop(step, args.steps, stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
+
+    # Dominant kernel (partial attention) and merge, each launched alone, back to back.
+    ms_partial = _time_loop(partial, args.steps, stream)
+    ms_merge = _time_loop(merge, args.steps, stream)
+    ms_cold = None
+    if not args.no_flush:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        ms_cold = _time_loop(step, max(3, min(args.steps, 10)), stream, flush)
+        del flush
+    torch.cuda.synchronize()
+
+    eb, fl = M.effective_bytes(wl), M.flops(wl)
+    gbs = eb / (ms_step * 1e-3) / 1e9
+    tfs = fl / (ms_step * 1e-3) / 1e12
+    bound = M.binding_roof(wl)
+    pk_bytes = M.partial_kernel_bytes(wl)
+    if bound == "hbm":
+        achieved = pk_bytes / (ms_partial * 1e-3) / 1e9
+        peak, unit = M.PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved = fl / (ms_partial * 1e-3) / 1e12
+        peak = M.PEAK_FP32_VECTOR_TFLOPS if wl.dtype == "float32" else M.PEAK_BF16_MFMA_TFLOPS
+        unit = "TFLOP/s"
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bfloat16" else "f32",
+        "data": "synthetic (seeded N(0,1) Q/K/V drawn on the device)",
+        "config": {"workload": wl.name, **{k_: v_ for k_, v_ in wl.summary().items() if k_ != "workload"}},
+        "tflops": round(tfs, 3),
+        "roofline_fraction_step": round(M.roofline_seconds(wl) / (ms_step * 1e-3), 4),
+        "binding_roof": bound,
+        "roofline": {
+            "kernel": "partial attention (splitkv_partial_attn)",
+            "bound": bound,
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": unit,
+            "frac": round(achieved / peak, 4),
+            "traffic": _traffic(args.workload),
+            "ms_per_launch": round(ms_partial, 5),
+            "algorithmic_bytes_per_launch": pk_bytes,
+        },
+        "ms_merge_kernel": round(ms_merge, 5),
+        "ms_per_step_cold_cache": None if ms_cold is None else round(ms_cold, 5),
+        "wall_ms_per_step": round(wall_ms, 5),
+        "effective_bytes": eb,
+        "flops": fl,
+        "lpt": {
+            "units": info["num_units"],
+            "workers": wl.num_workers,
+            "imbalance": info["imbalance"],
+            "makespan": info["makespan"],
+            "lower_bound": info["lower_bound"],
+            "plan_ms_median": round(plan_times[len(plan_times) // 2], 4),
+        },
+        "workspace_bytes": info["workspace_bytes"],
+        "kernel_sha": _kernel_sha(),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,183 @@
+/*
+ * splitkv.h -- C ABI of libsplitkv: exact split-KV attention on AMD MI355X (gfx950).
+ *
+ * The problem (Split-KV page, lede and "Timeline"): queries are a short block of
+ * trailing tokens; keys/values are a long context kept where they are and cut into
+ * context KV blocks; each block produces a result the size of the queries; the
+ * results combine into exactly the unsharded attention; blocks are placed on
+ * workers by a cost-aware longest-processing-time-first (LPT) plan whose load
+ * imbalance the method reports. On one GPU the workers are workgroups, one per
+ * compute unit.
+ *
+ * The pages print no formulas; this library uses the textbook ones:
+ *   query row i of sequence s sits at position p_i = n_s - q_s + i and, with the
+ *   causal mask, sees keys 0..p_i (bottom-right alignment); score = scale * <q, k>;
+ *   query head h reads KV head h / (Hq / Hkv); a block's partial is
+ *   O_b = sum_j e^{s_j} v_j / sum_j e^{s_j} and LSE_b = ln sum_j e^{s_j} over the
+ *   block's visible keys (O_b = 0, LSE_b = -inf when none is visible); the merge is
+ *   M = max_b LSE_b, w_b = e^{LSE_b - M}, O = sum_b w_b O_b / sum_b w_b,
+ *   LSE = M + ln sum_b w_b (natural log), which equals unsharded softmax attention.
+ *
+ * Conventions
+ *   - Every function returns an int status: SPLITKV_OK (0) or a negative error.
+ *     Argument errors are reported before any HIP call is made.
+ *   - Device memory (Q, K, V, plan buffer, workspace, outputs) is owned by the
+ *     caller. The library never allocates or frees device memory and never
+ *     synchronises a stream: kernels are enqueued on the caller's stream and
+ *     execution errors surface at the caller's next synchronisation.
+ *   - Plans are library-owned host objects (splitkv_plan_t, made by splitkv_plan, released by splitkv_plan_destroy).
+ *   - Functions are thread-safe for distinct plans; splitkv_last_error() is per thread.
+ *
+ * Layouts (all packed by sequence, in batch order)
+ *   Q   [sum_s q_s, Hq,  D]  element (t, h, d) at q + t*q_stride_tok + h*q_stride_head + d
+ *   K,V [sum_s n_s, Hkv, D]  likewise with their own strides; d is contiguous
+ *   out [sum_s q_s, Hq,  D]  fp32, contiguous
+ *   lse [sum_s q_s, Hq]      fp32, natural log, contiguous
+ *   Workspace (fp32): partial outputs first, then partial LSEs at byte offset
+ *   info.ws_lse_offset. The partial of unit (s, b, kv head k) for query row
+ *   r = i*g + (h - k*g) (query token i, query head h) is row
+ *       R = seq_row_base[s] + (k * nb_s + b) * (q_s * g) + r
+ *   with nb_s = ceil(n_s / B), g = Hq / Hkv and seq_row_base[s] the sum over earlier
+ *   sequences of nb_t * Hkv * q_t * g; its output is ws[R*D .. R*D + D) and its
+ *   LSE is ws_lse[R].
+ */
+#ifndef SPLITKV_H
+#define SPLITKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPLITKV_VERSION_MAJOR 0
+#define SPLITKV_VERSION_MINOR 1
+
+typedef enum {
+  SPLITKV_OK = 0,
+  SPLITKV_ERR_INVALID_ARG = -1, /* malformed problem, null pointer, bad stride or size   */
+  SPLITKV_ERR_UNSUPPORTED = -2, /* valid but without a kernel (dtype/head_dim combination) */
+  SPLITKV_ERR_WORKSPACE = -3,   /* workspace or plan buffer smaller than required         */
+  SPLITKV_ERR_HIP = -4,         /* a HIP runtime call failed; text in splitkv_last_error  */
+  SPLITKV_ERR_ALLOC = -5        /* host allocation failed                                 */
+} splitkv_status;
+
+typedef enum { SPLITKV_F32 = 0, SPLITKV_BF16 = 1 } splitkv_dtype;
+
+/* What one LPT unit covers. The Split-KV page places "context KV blocks"; a block of
+ * one KV head is the default unit (it serves g = Hq/Hkv query heads), a whole block
+ * serving all Hq query heads is the coarser alternative. */
+typedef enum { SPLITKV_UNIT_SEQ_BLOCK_KVHEAD = 0, SPLITKV_UNIT_SEQ_BLOCK = 1 } splitkv_granularity;
+
+/* Problem description. Host memory, caller-owned, read only during splitkv_plan. */
+typedef struct {
+  int32_t batch;            /* S >= 1 sequences                                      */
+  const int64_t *kv_lens;   /* [S] context lengths n_s, n_s >= q_s                   */
+  const int32_t *q_lens;    /* [S] trailing query counts q_s >= 1                    */
+  int32_t num_q_heads;      /* Hq >= 1                                               */
+  int32_t num_kv_heads;     /* Hkv >= 1, Hq % Hkv == 0                               */
+  int32_t head_dim;         /* D; kernels exist for 64 and 128                      */
+  int32_t block_len;        /* B >= 1 tokens per context KV block (last one ragged)  */
+  int32_t num_workers;      /* m >= 1 LPT workers = workgroups of the attention launch */
+  int32_t causal;           /* 1: bottom-right causal mask on the trailing queries   */
+  int32_t granularity;      /* splitkv_granularity                                   */
+} splitkv_problem;
+
+typedef struct splitkv_plan_s splitkv_plan_t; /* opaque, library-owned host object */
+
+typedef struct {
+  int64_t num_units;      /* LPT units                                                 */
+  int64_t total_cost;     /* sum of unit costs q_s * len * heads                       */
+  int64_t makespan;       /* largest worker load                                       */
+  int64_t lower_bound;    /* max(ceil(total/m), largest unit cost)                     */
+  double imbalance;       /* (m * makespan - total) / total, one float64 division      */
+  int64_t total_q;        /* sum_s q_s                                                 */
+  int64_t total_kv;       /* sum_s n_s                                                 */
+  int64_t partial_rows;   /* workspace rows: sum_s nb_s * Hkv * q_s * g                */
+  size_t plan_bytes;      /* device plan buffer size for splitkv_plan_upload           */
+  size_t workspace_bytes; /* workspace size for partial_attn / merge / attn            */
+  size_t ws_lse_offset;   /* byte offset of the partial LSEs inside the workspace      */
+} splitkv_plan_info;
+
+/* Device inputs. Pointers are device memory, caller-owned, read only. Strides are in
+ * elements; the innermost (head_dim) stride is 1. Base pointers must be 16-byte
+ * aligned and strides multiples of 16 bytes' worth of elements. */
+typedef struct {
+  const void *q, *k, *v;
+  int64_t q_stride_tok, q_stride_head;
+  int64_t k_stride_tok, k_stride_head;
+  int64_t v_stride_tok, v_stride_head;
+  int32_t dtype;  /* splitkv_dtype, the same for q, k and v                          */
+  float scale;    /* softmax scale; 0 selects 1/sqrt(head_dim)                       */
+} splitkv_inputs;
+
+/* Version as (major << 16) | minor. */
+int splitkv_version(void);
+
+/* Build the LPT plan on the host (no HIP call). Split-KV page, "Timeline": context KV
+ * blocks are allocated by a cost-aware LPT. Units are enumerated (seq, block, kv head)
+ * lexicographically, cost = q_s * len * heads served, stable sort by cost descending,
+ * each unit to the least-loaded worker (ties to the lowest index). On success *out is
+ * a new plan the caller releases with splitkv_plan_destroy.
+ * Errors: INVALID_ARG (null pointers, S < 1, q_s < 1, n_s < q_s, Hq % Hkv != 0,
+ * B < 1, m < 1, bad granularity), ALLOC. */
+int splitkv_plan(const splitkv_problem *problem, splitkv_plan_t **out);
+
+/* Plan statistics and buffer sizes. Errors: INVALID_ARG. */
+int splitkv_plan_info_get(const splitkv_plan_t *plan, splitkv_plan_info *info);
+
+/* Copy the plan out for inspection (host arrays, caller-owned; any may be NULL):
+ * unit_seq/unit_block/unit_kv_head/unit_len/unit_cost [num_units] in enumeration
+ * order (kv head -1 for whole-block units), worker_of [num_units],
+ * worker_ptr [m + 1] and worker_units [num_units] (each worker's units in the order
+ * it received them), load [m]. Errors: INVALID_ARG. */
+int splitkv_plan_export(const splitkv_plan_t *plan, int32_t *unit_seq, int32_t *unit_block,
+                        int32_t *unit_kv_head, int32_t *unit_len, int64_t *unit_cost,
+                        int32_t *worker_of, int32_t *worker_ptr, int32_t *worker_units,
+                        int64_t *load);
+
+/* Copy the plan's device image (plan_bytes) to caller-owned device memory dev_plan
+ * with an asynchronous host-to-device copy on hip_stream (NULL = default stream).
+ * The plan must stay alive until that copy has completed.
+ * Errors: INVALID_ARG, WORKSPACE (bytes < plan_bytes), HIP. */
+int splitkv_plan_upload(const splitkv_plan_t *plan, void *dev_plan, size_t bytes, void *hip_stream);
+
+/* Release a plan (NULL is ignored). */
+void splitkv_plan_destroy(splitkv_plan_t *plan);
+
+/* Partial attention of every unit: for each context KV block and KV head, the output
+ * and log-sum-exp of the queries against that block alone (the query-sized per-block
+ * result of the Split-KV page's lede). One workgroup per LPT worker walks its unit
+ * list. Writes the whole workspace (layout above); every row is written, rows that
+ * see no key of a block get O = 0 and LSE = -inf.
+ * Errors: INVALID_ARG (null/misaligned pointers, strides), UNSUPPORTED (no kernel for
+ * dtype/head_dim), WORKSPACE (ws_bytes < workspace_bytes), HIP (launch failed). */
+int splitkv_partial_attn(const splitkv_plan_t *plan, const void *dev_plan, const splitkv_inputs *in,
+                         float *ws, size_t ws_bytes, void *hip_stream);
+
+/* Log-sum-exp merge of the partials in the workspace into out [sum q, Hq, D] and
+ * lse [sum q, Hq] (fp32). Blocks are combined in block order, so the result does not
+ * depend on the plan's worker count. The Split-KV page ("Timeline") states that the
+ * method is exact: this merge reproduces unsharded attention up to rounding.
+ * Errors: INVALID_ARG, WORKSPACE, HIP. */
+int splitkv_merge(const splitkv_plan_t *plan, const void *dev_plan, const float *ws, size_t ws_bytes,
+                  float *out, float *lse, void *hip_stream);
+
+/* Fused call: partial attention and merge enqueued back to back on hip_stream, with
+ * sequences of a single block written straight to out/lse. Same arguments and errors
+ * as the two calls above. */
+int splitkv_attn(const splitkv_plan_t *plan, const void *dev_plan, const splitkv_inputs *in,
+                 float *ws, size_t ws_bytes, float *out, float *lse, void *hip_stream);
+
+/* Static text for a status code. */
+const char *splitkv_status_string(int status);
+
+/* Detail text of the last error on the calling thread ("" if none). */
+const char *splitkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLITKV_H */

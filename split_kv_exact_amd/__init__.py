@@ -1,0 +1,21 @@
+"""Exact split-KV attention for AMD MI355X (gfx950).
+
+The computation lives in ``libsplitkv.so`` (C ABI, ``include/splitkv.h``): an LPT
+planner on the host and HIP kernels for per-block partial attention, the
+log-sum-exp merge, and the fused call. This package is its ctypes binding.
+"""
+
+from .api import (  # noqa: F401
+    Plan,
+    SplitKVError,
+    plan_for,
+    splitkv_attn,
+    splitkv_merge,
+    splitkv_partial_attn,
+    splitkv_plan,
+    splitkv_plan_upload,
+    status_string,
+    version,
+    workspace,
+    workspace_views,
+)

@@ -1,0 +1,263 @@
+// C ABI of libsplitkv: argument checks, plan handling and kernel dispatch.
+//
+// Every argument check happens before any HIP call, so malformed calls fail the same
+// way with or without a GPU. The library allocates no device memory and never
+// synchronises a stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "kernels.hpp"
+#include "plan.hpp"
+#include "splitkv.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_plan(const splitkv_plan_t* pl, const void* dev_plan) {
+  if (!pl) return fail(SPLITKV_ERR_INVALID_ARG, "plan is NULL");
+  if (!dev_plan) return fail(SPLITKV_ERR_INVALID_ARG, "dev_plan is NULL");
+  if (!aligned16(dev_plan)) return fail(SPLITKV_ERR_INVALID_ARG, "dev_plan must be 16-byte aligned");
+  return SPLITKV_OK;
+}
+
+int check_inputs(const splitkv_plan_t* pl, const splitkv_inputs* in, float* scale_out) {
+  if (!in) return fail(SPLITKV_ERR_INVALID_ARG, "inputs is NULL");
+  if (in->dtype != SPLITKV_F32 && in->dtype != SPLITKV_BF16) return fail(SPLITKV_ERR_INVALID_ARG, "unknown dtype");
+  if (pl->D != 64 && pl->D != 128)
+    return fail(SPLITKV_ERR_UNSUPPORTED, "kernels exist for head_dim 64 and 128 only");
+  if (!in->q || !in->k || !in->v) return fail(SPLITKV_ERR_INVALID_ARG, "q, k and v must be non-NULL");
+  if (!aligned16(in->q) || !aligned16(in->k) || !aligned16(in->v))
+    return fail(SPLITKV_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
+  const int64_t vec = in->dtype == SPLITKV_F32 ? 4 : 8;  // elements per 16 bytes
+  const int64_t st[6] = {in->q_stride_tok, in->q_stride_head, in->k_stride_tok,
+                         in->k_stride_head, in->v_stride_tok, in->v_stride_head};
+  for (int64_t x : st)
+    if (x < 0 || x % vec != 0)
+      return fail(SPLITKV_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
+  if (!(std::isfinite(in->scale)) || in->scale < 0.f)
+    return fail(SPLITKV_ERR_INVALID_ARG, "scale must be finite and >= 0 (0 selects 1/sqrt(head_dim))");
+  *scale_out = in->scale == 0.f ? float(1.0 / std::sqrt(double(pl->D))) : in->scale;
+  return SPLITKV_OK;
+}
+
+int check_ws(const splitkv_plan_t* pl, const void* ws, size_t ws_bytes) {
+  if (!ws) return fail(SPLITKV_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned16(ws)) return fail(SPLITKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (ws_bytes < pl->ws_bytes)
+    return fail(SPLITKV_ERR_WORKSPACE, "workspace needs " + std::to_string(pl->ws_bytes) + " bytes, got " +
+                                           std::to_string(ws_bytes));
+  return SPLITKV_OK;
+}
+
+int check_out(const float* out, const float* lse) {
+  if (!out || !lse) return fail(SPLITKV_ERR_INVALID_ARG, "out and lse must be non-NULL");
+  if (!aligned16(out)) return fail(SPLITKV_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return fail(SPLITKV_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  return SPLITKV_OK;
+}
+
+splitkv::PartialArgs partial_args(const splitkv_plan_t* pl, const void* dev_plan, const splitkv_inputs* in,
+                                  float scale, float* ws) {
+  const uint8_t* base = static_cast<const uint8_t*>(dev_plan);
+  splitkv::PartialArgs a{};
+  a.q = in->q;
+  a.k = in->k;
+  a.v = in->v;
+  a.q_st = in->q_stride_tok;
+  a.q_sh = in->q_stride_head;
+  a.k_st = in->k_stride_tok;
+  a.k_sh = in->k_stride_head;
+  a.v_st = in->v_stride_tok;
+  a.v_sh = in->v_stride_head;
+  a.scale = scale;
+  a.seqs = reinterpret_cast<const splitkv::SeqRec*>(base + pl->layout.seqs);
+  a.units = reinterpret_cast<const splitkv::UnitRec*>(base + pl->layout.units);
+  a.worker_ptr = reinterpret_cast<const int32_t*>(base + pl->layout.worker_ptr);
+  a.num_workers = pl->m;
+  a.Hq = pl->Hq;
+  a.Hkv = pl->Hkv;
+  a.g = pl->g;
+  a.B = pl->B;
+  a.causal = pl->causal;
+  a.ws_o = ws;
+  a.ws_lse = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + pl->ws_lse_offset);
+  a.out = nullptr;
+  a.lse = nullptr;
+  return a;
+}
+
+splitkv::MergeArgs merge_args(const splitkv_plan_t* pl, const void* dev_plan, const float* ws, float* out, float* lse,
+                              bool multi_only) {
+  const uint8_t* base = static_cast<const uint8_t*>(dev_plan);
+  splitkv::MergeArgs m{};
+  m.seqs = reinterpret_cast<const splitkv::SeqRec*>(base + pl->layout.seqs);
+  if (multi_only) {
+    m.seq_ids = reinterpret_cast<const int32_t*>(base + pl->layout.merge_multi);
+    m.row_base = reinterpret_cast<const int64_t*>(base + pl->layout.merge_multi_base);
+    m.count = pl->num_multi;
+    m.total_rows = pl->merge_rows_multi;
+  } else {
+    m.seq_ids = nullptr;
+    m.row_base = reinterpret_cast<const int64_t*>(base + pl->layout.merge_all);
+    m.count = pl->S;
+    m.total_rows = pl->merge_rows_all;
+  }
+  m.Hq = pl->Hq;
+  m.Hkv = pl->Hkv;
+  m.g = pl->g;
+  m.ws_o = ws;
+  m.ws_lse = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(ws) + pl->ws_lse_offset);
+  m.out = out;
+  m.lse = lse;
+  return m;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SPLITKV_OK;
+  return fail(SPLITKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int launch_partial(const splitkv_plan_t* pl, const splitkv::PartialArgs& a, int dtype, hipStream_t stream) {
+  hipError_t e = dtype == SPLITKV_BF16 ? splitkv::launch_partial_bf16(a, pl->D, stream)
+                                       : splitkv::launch_partial_f32(a, pl->D, stream);
+  return hip_status(e, "partial attention launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int splitkv_version(void) { return (SPLITKV_VERSION_MAJOR << 16) | SPLITKV_VERSION_MINOR; }
+
+int splitkv_plan(const splitkv_problem* problem, splitkv_plan_t** out) {
+  g_last_error.clear();
+  if (!out) return fail(SPLITKV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  std::string why;
+  if (!splitkv::validate_problem(problem, &why)) return fail(SPLITKV_ERR_INVALID_ARG, why);
+  splitkv_plan_t* pl = nullptr;
+  try {
+    pl = new splitkv_plan_t();
+    splitkv::build_plan(problem, pl);
+  } catch (const std::bad_alloc&) {
+    delete pl;
+    return fail(SPLITKV_ERR_ALLOC, "host allocation failed while planning");
+  }
+  *out = pl;
+  return SPLITKV_OK;
+}
+
+int splitkv_plan_info_get(const splitkv_plan_t* pl, splitkv_plan_info* info) {
+  g_last_error.clear();
+  if (!pl || !info) return fail(SPLITKV_ERR_INVALID_ARG, "plan and info must be non-NULL");
+  info->num_units = int64_t(pl->u_cost.size());
+  info->total_cost = pl->total_cost;
+  info->makespan = pl->makespan;
+  info->lower_bound = pl->lower_bound;
+  info->imbalance = pl->imbalance;
+  info->total_q = pl->total_q;
+  info->total_kv = pl->total_kv;
+  info->partial_rows = pl->partial_rows;
+  info->plan_bytes = pl->image.size();
+  info->workspace_bytes = pl->ws_bytes;
+  info->ws_lse_offset = pl->ws_lse_offset;
+  return SPLITKV_OK;
+}
+
+int splitkv_plan_export(const splitkv_plan_t* pl, int32_t* unit_seq, int32_t* unit_block, int32_t* unit_kv_head,
+                        int32_t* unit_len, int64_t* unit_cost, int32_t* worker_of, int32_t* worker_ptr,
+                        int32_t* worker_units, int64_t* load) {
+  g_last_error.clear();
+  if (!pl) return fail(SPLITKV_ERR_INVALID_ARG, "plan is NULL");
+  const size_t n = pl->u_cost.size();
+  if (unit_seq) std::memcpy(unit_seq, pl->u_seq.data(), n * sizeof(int32_t));
+  if (unit_block) std::memcpy(unit_block, pl->u_block.data(), n * sizeof(int32_t));
+  if (unit_kv_head) std::memcpy(unit_kv_head, pl->u_kv.data(), n * sizeof(int32_t));
+  if (unit_len) std::memcpy(unit_len, pl->u_len.data(), n * sizeof(int32_t));
+  if (unit_cost) std::memcpy(unit_cost, pl->u_cost.data(), n * sizeof(int64_t));
+  if (worker_of) std::memcpy(worker_of, pl->worker_of.data(), n * sizeof(int32_t));
+  if (worker_ptr) std::memcpy(worker_ptr, pl->worker_ptr.data(), pl->worker_ptr.size() * sizeof(int32_t));
+  if (worker_units) std::memcpy(worker_units, pl->worker_units.data(), n * sizeof(int32_t));
+  if (load) std::memcpy(load, pl->load.data(), pl->load.size() * sizeof(int64_t));
+  return SPLITKV_OK;
+}
+
+int splitkv_plan_upload(const splitkv_plan_t* pl, void* dev_plan, size_t bytes, void* hip_stream) {
+  g_last_error.clear();
+  if (int st = check_plan(pl, dev_plan)) return st;
+  if (bytes < pl->image.size())
+    return fail(SPLITKV_ERR_WORKSPACE, "plan buffer needs " + std::to_string(pl->image.size()) + " bytes");
+  return hip_status(hipMemcpyAsync(dev_plan, pl->image.data(), pl->image.size(), hipMemcpyHostToDevice,
+                                   static_cast<hipStream_t>(hip_stream)),
+                    "plan upload");
+}
+
+void splitkv_plan_destroy(splitkv_plan_t* pl) { delete pl; }
+
+int splitkv_partial_attn(const splitkv_plan_t* pl, const void* dev_plan, const splitkv_inputs* in, float* ws,
+                         size_t ws_bytes, void* hip_stream) {
+  g_last_error.clear();
+  if (int st = check_plan(pl, dev_plan)) return st;
+  float scale = 0.f;
+  if (int st = check_inputs(pl, in, &scale)) return st;
+  if (int st = check_ws(pl, ws, ws_bytes)) return st;
+  const splitkv::PartialArgs a = partial_args(pl, dev_plan, in, scale, ws);
+  return launch_partial(pl, a, in->dtype, static_cast<hipStream_t>(hip_stream));
+}
+
+int splitkv_merge(const splitkv_plan_t* pl, const void* dev_plan, const float* ws, size_t ws_bytes, float* out,
+                  float* lse, void* hip_stream) {
+  g_last_error.clear();
+  if (int st = check_plan(pl, dev_plan)) return st;
+  if (pl->D != 64 && pl->D != 128)
+    return fail(SPLITKV_ERR_UNSUPPORTED, "kernels exist for head_dim 64 and 128 only");
+  if (int st = check_ws(pl, ws, ws_bytes)) return st;
+  if (int st = check_out(out, lse)) return st;
+  const splitkv::MergeArgs m = merge_args(pl, dev_plan, ws, out, lse, false);
+  return hip_status(splitkv::launch_merge(m, pl->D, static_cast<hipStream_t>(hip_stream)), "merge launch");
+}
+
+int splitkv_attn(const splitkv_plan_t* pl, const void* dev_plan, const splitkv_inputs* in, float* ws, size_t ws_bytes,
+                 float* out, float* lse, void* hip_stream) {
+  g_last_error.clear();
+  if (int st = check_plan(pl, dev_plan)) return st;
+  float scale = 0.f;
+  if (int st = check_inputs(pl, in, &scale)) return st;
+  if (int st = check_ws(pl, ws, ws_bytes)) return st;
+  if (int st = check_out(out, lse)) return st;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  splitkv::PartialArgs a = partial_args(pl, dev_plan, in, scale, ws);
+  a.out = out;
+  a.lse = lse;
+  if (int st = launch_partial(pl, a, in->dtype, stream)) return st;
+  const splitkv::MergeArgs m = merge_args(pl, dev_plan, ws, out, lse, true);
+  return hip_status(splitkv::launch_merge(m, pl->D, stream), "merge launch");
+}
+
+const char* splitkv_status_string(int status) {
+  switch (status) {
+    case SPLITKV_OK: return "ok";
+    case SPLITKV_ERR_INVALID_ARG: return "invalid argument";
+    case SPLITKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SPLITKV_ERR_WORKSPACE: return "buffer too small";
+    case SPLITKV_ERR_HIP: return "HIP runtime error";
+    case SPLITKV_ERR_ALLOC: return "host allocation failed";
+    default: return "unknown status";
+  }
+}
+
+const char* splitkv_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

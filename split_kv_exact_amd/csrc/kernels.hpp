@@ -1,0 +1,49 @@
+// Internal launch interface between the C ABI layer and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan_image.hpp"
+
+namespace splitkv {
+
+// Arguments of the partial-attention kernels (one workgroup per LPT worker).
+struct PartialArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh;  // strides in elements
+  float scale;                                 // softmax scale
+  const SeqRec* seqs;
+  const UnitRec* units;
+  const int32_t* worker_ptr;
+  int32_t num_workers;
+  int32_t Hq, Hkv, g, B, causal;
+  float* ws_o;    // partial outputs [partial_rows, D]
+  float* ws_lse;  // partial LSEs [partial_rows]
+  // When non-null, sequences with a single block write their final result here
+  // instead of the workspace (the fused path).
+  float* out;
+  float* lse;
+};
+
+// Arguments of the merge kernel (one wavefront per merged row).
+struct MergeArgs {
+  const SeqRec* seqs;
+  const int32_t* seq_ids;    // sequences to merge (null: all sequences 0..count-1)
+  const int64_t* row_base;   // prefix over those sequences of Hkv * rows
+  int32_t count;             // number of sequences to merge
+  int64_t total_rows;        // row_base[count]
+  int32_t Hq, Hkv, g;
+  float scale;
+  const float* ws_o;
+  const float* ws_lse;
+  float* out;
+  float* lse;
+};
+
+hipError_t launch_partial_bf16(const PartialArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_partial_f32(const PartialArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
+
+}  // namespace splitkv

@@ -1,0 +1,226 @@
+// Cost-aware LPT placement of context KV blocks on workers (host code only).
+//
+// Split-KV page, "Timeline": context KV blocks are allocated by a cost-aware
+// longest-processing-time-first strategy with a reported load imbalance below 1%.
+// The page gives no cost model, tie-break or imbalance definition; this planner uses
+//   unit       = (sequence, block, KV head), enumerated in that order (or a whole
+//                (sequence, block) serving every query head: the coarse granularity);
+//   cost       = q_s * block length * query heads served (exact int64);
+//   order      = costs descending, ties in enumeration order (stable sort);
+//   placement  = worker with the smallest (load, index) via a binary min-heap;
+//   imbalance  = (m * max_load - total) / total, one float64 division.
+// With these rules the plan is unique, so it can be compared bit for bit.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cstring>
+#include <functional>
+#include <numeric>
+#include <queue>
+#include <utility>
+
+namespace splitkv {
+
+static inline uint64_t align16(uint64_t x) { return (x + 15) & ~uint64_t(15); }
+
+bool validate_problem(const splitkv_problem* p, std::string* why) {
+  auto fail = [&](const char* msg) {
+    *why = msg;
+    return false;
+  };
+  if (!p) return fail("problem is NULL");
+  if (p->batch < 1) return fail("batch must be >= 1");
+  if (!p->kv_lens || !p->q_lens) return fail("kv_lens and q_lens must be non-NULL");
+  if (p->num_q_heads < 1 || p->num_kv_heads < 1) return fail("head counts must be >= 1");
+  if (p->num_q_heads % p->num_kv_heads != 0) return fail("num_q_heads must be a multiple of num_kv_heads");
+  if (p->head_dim < 1) return fail("head_dim must be >= 1");
+  if (p->block_len < 1 || p->block_len > (1 << 30)) return fail("block_len must be in [1, 2^30]");
+  if (p->num_workers < 1) return fail("num_workers must be >= 1");
+  if (p->causal != 0 && p->causal != 1) return fail("causal must be 0 or 1");
+  if (p->granularity != SPLITKV_UNIT_SEQ_BLOCK_KVHEAD && p->granularity != SPLITKV_UNIT_SEQ_BLOCK)
+    return fail("unknown granularity");
+  const int64_t g = p->num_q_heads / p->num_kv_heads;
+  for (int32_t s = 0; s < p->batch; ++s) {
+    if (p->q_lens[s] < 1) return fail("every q_len must be >= 1");
+    if (p->kv_lens[s] < p->q_lens[s]) return fail("every kv_len must be >= its q_len");
+    if (p->kv_lens[s] > (int64_t(1) << 40)) return fail("kv_len too large");
+    // Keep per-unit row counts in int32 and per-unit costs far from int64 overflow.
+    if (int64_t(p->q_lens[s]) * g > (int64_t(1) << 30)) return fail("q_len * group too large");
+  }
+  return true;
+}
+
+void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
+  pl->S = p->batch;
+  pl->Hq = p->num_q_heads;
+  pl->Hkv = p->num_kv_heads;
+  pl->D = p->head_dim;
+  pl->B = p->block_len;
+  pl->m = p->num_workers;
+  pl->causal = p->causal;
+  pl->granularity = p->granularity;
+  pl->g = p->num_q_heads / p->num_kv_heads;
+  pl->kv_lens.assign(p->kv_lens, p->kv_lens + p->batch);
+  pl->q_lens.assign(p->q_lens, p->q_lens + p->batch);
+
+  const int32_t S = pl->S, Hkv = pl->Hkv, g = pl->g, B = pl->B, m = pl->m;
+  const bool per_head = pl->granularity == SPLITKV_UNIT_SEQ_BLOCK_KVHEAD;
+  const int64_t heads = per_head ? g : pl->Hq;
+
+  // Sequence records and workspace layout.
+  pl->seqs.resize(S);
+  int64_t kv_base = 0, q_base = 0, row_base = 0;
+  pl->merge_rows_all = 0;
+  pl->merge_rows_multi = 0;
+  pl->num_multi = 0;
+  pl->max_rows = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    SeqRec& r = pl->seqs[s];
+    r.kv_base = kv_base;
+    r.q_base = q_base;
+    r.n = pl->kv_lens[s];
+    r.row_base = row_base;
+    r.q = pl->q_lens[s];
+    r.nb = int32_t((r.n + B - 1) / B);
+    r.rows = r.q * g;
+    r.pad = 0;
+    kv_base += r.n;
+    q_base += r.q;
+    row_base += int64_t(r.nb) * Hkv * r.rows;
+    pl->merge_rows_all += int64_t(Hkv) * r.rows;
+    if (r.nb > 1) {
+      pl->merge_rows_multi += int64_t(Hkv) * r.rows;
+      pl->num_multi++;
+    }
+    pl->max_rows = std::max(pl->max_rows, r.rows);
+  }
+  pl->total_kv = kv_base;
+  pl->total_q = q_base;
+  pl->partial_rows = row_base;
+  pl->ws_lse_offset = align16(uint64_t(row_base) * pl->D * sizeof(float));
+  pl->ws_bytes = pl->ws_lse_offset + align16(uint64_t(row_base) * sizeof(float));
+
+  // Units in enumeration order, with their costs.
+  pl->u_seq.clear();
+  pl->u_block.clear();
+  pl->u_kv.clear();
+  pl->u_len.clear();
+  pl->u_cost.clear();
+  for (int32_t s = 0; s < S; ++s) {
+    const SeqRec& r = pl->seqs[s];
+    for (int32_t b = 0; b < r.nb; ++b) {
+      const int32_t len = int32_t(std::min<int64_t>(B, r.n - int64_t(b) * B));
+      const int64_t cost = int64_t(r.q) * len * heads;
+      if (per_head) {
+        for (int32_t k = 0; k < Hkv; ++k) {
+          pl->u_seq.push_back(s);
+          pl->u_block.push_back(b);
+          pl->u_kv.push_back(k);
+          pl->u_len.push_back(len);
+          pl->u_cost.push_back(cost);
+        }
+      } else {
+        pl->u_seq.push_back(s);
+        pl->u_block.push_back(b);
+        pl->u_kv.push_back(-1);
+        pl->u_len.push_back(len);
+        pl->u_cost.push_back(cost);
+      }
+    }
+  }
+  const int64_t n = int64_t(pl->u_cost.size());
+
+  // LPT: stable sort by cost descending, then least-loaded worker (lowest index on ties).
+  std::vector<int32_t> order(n);
+  std::iota(order.begin(), order.end(), 0);
+  const std::vector<int64_t>& cost = pl->u_cost;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return cost[a] > cost[b]; });
+
+  using Entry = std::pair<int64_t, int32_t>;  // (load, worker): lexicographic min = least load, lowest index
+  std::vector<Entry> heap_storage;
+  heap_storage.reserve(m);
+  for (int32_t w = 0; w < m; ++w) heap_storage.emplace_back(0, w);
+  std::priority_queue<Entry, std::vector<Entry>, std::greater<Entry>> heap(std::greater<Entry>(),
+                                                                           std::move(heap_storage));
+  pl->worker_of.assign(n, -1);
+  pl->load.assign(m, 0);
+  std::vector<std::vector<int32_t>> lists(m);
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t u = order[i];
+    Entry e = heap.top();
+    heap.pop();
+    const int32_t w = e.second;
+    pl->worker_of[u] = w;
+    lists[w].push_back(u);
+    pl->load[w] = e.first + cost[u];
+    heap.emplace(pl->load[w], w);
+  }
+  pl->worker_ptr.assign(m + 1, 0);
+  pl->worker_units.clear();
+  pl->worker_units.reserve(n);
+  for (int32_t w = 0; w < m; ++w) {
+    pl->worker_units.insert(pl->worker_units.end(), lists[w].begin(), lists[w].end());
+    pl->worker_ptr[w + 1] = int32_t(pl->worker_units.size());
+  }
+
+  // Statistics.
+  pl->total_cost = 0;
+  int64_t max_cost = 0;
+  for (int64_t c : cost) {
+    pl->total_cost += c;
+    max_cost = std::max(max_cost, c);
+  }
+  pl->makespan = 0;
+  for (int64_t l : pl->load) pl->makespan = std::max(pl->makespan, l);
+  pl->lower_bound = std::max<int64_t>((pl->total_cost + m - 1) / m, max_cost);
+  pl->imbalance = pl->total_cost == 0
+                      ? 0.0
+                      : double(int64_t(m) * pl->makespan - pl->total_cost) / double(pl->total_cost);
+
+  // Device image.
+  ImageLayout& L = pl->layout;
+  uint64_t off = 0;
+  L.seqs = off;
+  off = align16(off + sizeof(SeqRec) * uint64_t(S));
+  L.units = off;
+  off = align16(off + sizeof(UnitRec) * uint64_t(n));
+  L.worker_ptr = off;
+  off = align16(off + sizeof(int32_t) * uint64_t(m + 1));
+  L.merge_all = off;
+  off = align16(off + sizeof(int64_t) * uint64_t(S + 1));
+  L.merge_multi = off;
+  off = align16(off + sizeof(int32_t) * uint64_t(std::max(pl->num_multi, 1)));
+  L.merge_multi_base = off;
+  off = align16(off + sizeof(int64_t) * uint64_t(pl->num_multi + 1));
+  L.total = off;
+
+  pl->image.assign(L.total, 0);
+  uint8_t* base = pl->image.data();
+  std::memcpy(base + L.seqs, pl->seqs.data(), sizeof(SeqRec) * S);
+  UnitRec* ur = reinterpret_cast<UnitRec*>(base + L.units);
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t u = pl->worker_units[i];
+    ur[i].seq = pl->u_seq[u];
+    ur[i].block = pl->u_block[u];
+    ur[i].kv0 = per_head ? pl->u_kv[u] : 0;
+    ur[i].nkv = per_head ? 1 : Hkv;
+  }
+  std::memcpy(base + L.worker_ptr, pl->worker_ptr.data(), sizeof(int32_t) * (m + 1));
+  int64_t* ma = reinterpret_cast<int64_t*>(base + L.merge_all);
+  int32_t* mm = reinterpret_cast<int32_t*>(base + L.merge_multi);
+  int64_t* mb = reinterpret_cast<int64_t*>(base + L.merge_multi_base);
+  ma[0] = 0;
+  mb[0] = 0;
+  int32_t j = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    const int64_t rows = int64_t(Hkv) * pl->seqs[s].rows;
+    ma[s + 1] = ma[s] + rows;
+    if (pl->seqs[s].nb > 1) {
+      mm[j] = s;
+      mb[j + 1] = mb[j] + rows;
+      ++j;
+    }
+  }
+}
+
+}  // namespace splitkv

@@ -1,0 +1,68 @@
+"""Byte and flop accounting for throughput reports (counting only).
+
+effective_bytes: what the whole split-KV attention must move at least once:
+    Q + K + V (each stored element counted once) + O (fp32) + LSE (fp32).
+partial_kernel_bytes: what one launch of the partial-attention kernel must move:
+    per unit (sequence s, block b, KV heads), the block's K and V, the unit's query
+    rows of Q, and its fp32 partial output and LSE.
+merge_kernel_bytes: partials read once, O and LSE written once.
+flops: 2 flops per multiply-add of QK^T and of PV over the (query, key) pairs the
+    mask keeps: 4 * D * Hq * sum_s visible_pairs_s.
+"""
+
+from __future__ import annotations
+
+# MI355X published peaks used for roofline fractions.
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_MFMA_TFLOPS = 2500.0
+PEAK_FP32_VECTOR_TFLOPS = 157.3
+
+
+def visible_pairs(wl) -> int:
+    tot = 0
+    for n, q in zip(wl.kv_lens, wl.q_lens):
+        tot += q * n - q * (q - 1) // 2 if wl.causal else q * n
+    return tot
+
+
+def flops(wl) -> int:
+    return 4 * wl.head_dim * wl.num_q_heads * visible_pairs(wl)
+
+
+def kv_bytes(wl) -> int:
+    return 2 * wl.total_kv * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+
+
+def q_bytes(wl) -> int:
+    return wl.total_q * wl.num_q_heads * wl.head_dim * wl.elem_bytes
+
+
+def out_bytes(wl) -> int:
+    return wl.total_q * wl.num_q_heads * (wl.head_dim + 1) * 4
+
+
+def effective_bytes(wl) -> int:
+    return q_bytes(wl) + kv_bytes(wl) + out_bytes(wl)
+
+
+def partial_rows(wl) -> int:
+    return sum(wl.num_blocks(s) * wl.num_kv_heads * wl.q_lens[s] * wl.group for s in range(wl.batch))
+
+
+def partial_kernel_bytes(wl) -> int:
+    q_per_unit = sum(wl.num_blocks(s) * wl.q_lens[s] * wl.num_q_heads for s in range(wl.batch))
+    return kv_bytes(wl) + q_per_unit * wl.head_dim * wl.elem_bytes + partial_rows(wl) * (wl.head_dim + 1) * 4
+
+
+def merge_kernel_bytes(wl) -> int:
+    return partial_rows(wl) * (wl.head_dim + 1) * 4 + out_bytes(wl)
+
+
+def roofline_seconds(wl) -> float:
+    peak_f = PEAK_FP32_VECTOR_TFLOPS if wl.dtype == "float32" else PEAK_BF16_MFMA_TFLOPS
+    return max(effective_bytes(wl) / (PEAK_HBM_GBS * 1e9), flops(wl) / (peak_f * 1e12))
+
+
+def binding_roof(wl) -> str:
+    peak_f = PEAK_FP32_VECTOR_TFLOPS if wl.dtype == "float32" else PEAK_BF16_MFMA_TFLOPS
+    return "hbm" if effective_bytes(wl) / (PEAK_HBM_GBS * 1e9) >= flops(wl) / (peak_f * 1e12) else "mfma"

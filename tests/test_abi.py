@@ -1,0 +1,162 @@
+"""C-ABI checks that need no GPU: exports, status strings and argument errors.
+
+Every argument error is reported before the library makes a HIP call, so these run
+on a machine without a GPU. Device pointers passed here are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from split_kv_exact_amd import _lib as L
+from split_kv_exact_amd import SplitKVError, splitkv_plan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "splitkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(splitkv_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    decl = declared_functions()
+    assert set(decl) == set(L.EXPORTED), decl
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    v = lib.splitkv_version()
+    assert v >> 16 == 0 and (v & 0xFFFF) >= 1
+    assert lib.splitkv_status_string(0) == b"ok"
+    for code in (-1, -2, -3, -4, -5):
+        s = lib.splitkv_status_string(code)
+        assert s and s != b"unknown status"
+    assert lib.splitkv_status_string(-99) == b"unknown status"
+
+
+def _problem(kv, q, hq=4, hkv=2, d=128, b=64, m=8, causal=1, gran=0):
+    kv = np.asarray(kv, np.int64)
+    q = np.asarray(q, np.int32)
+    p = L.Problem(batch=len(kv), kv_lens=kv.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                  q_lens=q.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), num_q_heads=hq, num_kv_heads=hkv,
+                  head_dim=d, block_len=b, num_workers=m, causal=causal, granularity=gran)
+    return p, (kv, q)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(kv=[10], q=[0]),            # q_len < 1
+    dict(kv=[3], q=[4]),             # kv_len < q_len
+    dict(kv=[10], q=[2], hq=6, hkv=4),  # Hq % Hkv != 0
+    dict(kv=[10], q=[2], b=0),       # block_len < 1
+    dict(kv=[10], q=[2], m=0),       # num_workers < 1
+    dict(kv=[10], q=[2], causal=2),
+    dict(kv=[10], q=[2], gran=7),
+    dict(kv=[10], q=[2], hq=0),
+])
+def test_invalid_problems_are_rejected(lib, kw):
+    p, keep = _problem(**kw)
+    h = ctypes.c_void_p(1234)
+    st = lib.splitkv_plan(ctypes.byref(p), ctypes.byref(h))
+    assert st == L.SPLITKV_ERR_INVALID_ARG
+    assert h.value is None
+    assert lib.splitkv_last_error()
+
+
+def test_null_arguments(lib):
+    h = ctypes.c_void_p()
+    assert lib.splitkv_plan(None, ctypes.byref(h)) == L.SPLITKV_ERR_INVALID_ARG
+    p, keep = _problem([10], [2])
+    assert lib.splitkv_plan(ctypes.byref(p), None) == L.SPLITKV_ERR_INVALID_ARG
+    p.batch = 0
+    assert lib.splitkv_plan(ctypes.byref(p), ctypes.byref(h)) == L.SPLITKV_ERR_INVALID_ARG
+    assert lib.splitkv_plan_info_get(None, ctypes.byref(L.PlanInfo())) == L.SPLITKV_ERR_INVALID_ARG
+    lib.splitkv_plan_destroy(None)  # ignored
+
+
+def test_python_binding_raises():
+    with pytest.raises(SplitKVError) as e:
+        splitkv_plan([5], [9], 4, 2, 128, 16, 4)
+    assert e.value.status == L.SPLITKV_ERR_INVALID_ARG
+    assert "kv_len" in str(e.value)
+
+
+FAKE = 1 << 20  # aligned, never dereferenced: every call below fails validation first
+
+
+def _plan_handle(lib, d=128):
+    p, keep = _problem([100, 40], [3, 1], d=d)
+    h = ctypes.c_void_p()
+    assert lib.splitkv_plan(ctypes.byref(p), ctypes.byref(h)) == 0
+    inf = L.PlanInfo()
+    assert lib.splitkv_plan_info_get(h, ctypes.byref(inf)) == 0
+    return h, inf
+
+
+def _inputs(dtype=L.SPLITKV_BF16, ptr=FAKE, strides=(256, 128, 256, 128, 256, 128), scale=0.0):
+    return L.Inputs(q=ptr, k=ptr, v=ptr, q_stride_tok=strides[0], q_stride_head=strides[1],
+                    k_stride_tok=strides[2], k_stride_head=strides[3], v_stride_tok=strides[4],
+                    v_stride_head=strides[5], dtype=dtype, scale=scale)
+
+
+def test_partial_attn_argument_errors(lib):
+    h, inf = _plan_handle(lib)
+    ws, nbytes = ctypes.c_void_p(FAKE), inf.workspace_bytes
+    dp = ctypes.c_void_p(FAKE)
+    good = _inputs()
+    f = lib.splitkv_partial_attn
+    assert f(None, dp, ctypes.byref(good), ws, nbytes, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, None, ctypes.byref(good), ws, nbytes, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, ctypes.c_void_p(FAKE + 4), ctypes.byref(good), ws, nbytes, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, dp, None, ws, nbytes, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, dp, ctypes.byref(_inputs(dtype=5)), ws, nbytes, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, dp, ctypes.byref(_inputs(ptr=0)), ws, nbytes, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, dp, ctypes.byref(_inputs(ptr=FAKE + 2)), ws, nbytes, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, dp, ctypes.byref(_inputs(strides=(256, 100, 256, 128, 256, 128))), ws, nbytes,
+             None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, dp, ctypes.byref(_inputs(scale=-1.0)), ws, nbytes, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, dp, ctypes.byref(_inputs(scale=float("nan"))), ws, nbytes, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, dp, ctypes.byref(good), None, nbytes, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, dp, ctypes.byref(good), ws, nbytes - 1, None) == L.SPLITKV_ERR_WORKSPACE
+    assert b"workspace needs" in lib.splitkv_last_error()
+    lib.splitkv_plan_destroy(h)
+
+
+def test_unsupported_head_dim(lib):
+    h, inf = _plan_handle(lib, d=96)
+    st = lib.splitkv_partial_attn(h, ctypes.c_void_p(FAKE), ctypes.byref(_inputs()), ctypes.c_void_p(FAKE),
+                                  inf.workspace_bytes, None)
+    assert st == L.SPLITKV_ERR_UNSUPPORTED
+    lib.splitkv_plan_destroy(h)
+
+
+def test_merge_and_attn_argument_errors(lib):
+    h, inf = _plan_handle(lib)
+    dp, ws, nbytes = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), inf.workspace_bytes
+    out, lse = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE)
+    assert lib.splitkv_merge(h, dp, ws, nbytes, None, lse, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert lib.splitkv_merge(h, dp, ws, nbytes, ctypes.c_void_p(FAKE + 8), lse, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert lib.splitkv_merge(h, dp, ws, 16, out, lse, None) == L.SPLITKV_ERR_WORKSPACE
+    good = _inputs()
+    assert lib.splitkv_attn(h, dp, ctypes.byref(good), ws, nbytes, out, None, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert lib.splitkv_attn(h, dp, ctypes.byref(good), ws, 0, out, lse, None) == L.SPLITKV_ERR_WORKSPACE
+    assert lib.splitkv_plan_upload(h, dp, inf.plan_bytes - 1, None) == L.SPLITKV_ERR_WORKSPACE
+    assert lib.splitkv_plan_upload(h, None, inf.plan_bytes, None) == L.SPLITKV_ERR_INVALID_ARG
+    lib.splitkv_plan_destroy(h)
+
+
+def test_plan_info_sizes():
+    pl = splitkv_plan([100, 40], [3, 1], 4, 2, 128, 64, 8)
+    inf = pl.info()
+    g = 2
+    rows = 2 * (2 * 3 * g) + 1 * (2 * 1 * g)  # nb * Hkv * q * g per sequence
+    assert inf["partial_rows"] == rows
+    assert inf["ws_lse_offset"] == rows * 128 * 4
+    assert inf["workspace_bytes"] >= rows * 129 * 4
+    assert inf["total_q"] == 4 and inf["total_kv"] == 140
+    assert inf["plan_bytes"] > 0 and inf["plan_bytes"] % 16 == 0

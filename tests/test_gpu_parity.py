@@ -1,0 +1,244 @@
+"""GPU parity: libsplitkv's HIP kernels against the float64 oracle (needs an MI355X).
+
+Small cases run the whole oracle (every output, every partial). The five workload
+shapes at full size are checked on sampled outputs and sampled partials, in the
+launch configuration the benchmark times (the fused call over the LPT plan).
+Inputs are drawn on the device and copied to the host for the oracle.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import split_kv_exact_amd as skv
+from oracle import attend_rows, attention_ref, partials_ref
+from tests.parity import Diff, assert_within, compare, offsets, partial_row, say, scale_of
+from workloads import Workload, get_workload, make_qkv, widen_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _wl(name, kv, q, hq, hkv, d, b, m, dtype="bfloat16", causal=True, gran=0, seed=7, boost_frac=0.0):
+    return Workload(name=name, dtype=dtype, kv_lens=tuple(kv), q_lens=tuple(q), num_q_heads=hq, num_kv_heads=hkv,
+                    head_dim=d, block_len=b, num_workers=m, causal=causal, seed=seed, boost_frac=boost_frac,
+                    boost=8.0, granularity=gran)
+
+
+SMALL = [
+    get_workload("small"),
+    _wl("ragged_bf16_d128", [1000, 333, 77, 2100, 16], [16, 5, 1, 40, 16], 32, 8, 128, 256, 16),
+    _wl("ragged_bf16_d64", [1000, 333, 77, 513], [16, 5, 1, 9], 8, 2, 64, 128, 7),
+    _wl("fp32_d128", [300, 129, 64], [7, 3, 64], 4, 2, 128, 64, 5, dtype="float32"),
+    _wl("noncausal_bf16", [700, 45], [12, 3], 16, 4, 128, 128, 9, causal=False),
+    _wl("noncausal_fp32_d64", [200, 45], [4, 3], 2, 1, 64, 64, 3, dtype="float32", causal=False),
+    _wl("whole_block_units", [900, 260], [8, 2], 16, 4, 128, 256, 6, gran=1),
+    _wl("edge_q_equals_n", [1, 5, 64, 2, 3], [1, 5, 64, 1, 3], 8, 4, 128, 16, 11),
+    _wl("block_longer_than_context", [100, 37], [3, 2], 8, 2, 128, 4096, 4),
+    _wl("boosted_keys", [3000, 1500], [16, 1], 64, 8, 128, 512, 32, boost_frac=0.01),
+    _wl("many_rows", [2048], [300], 32, 8, 128, 512, 8),
+    _wl("more_workers_than_units", [300], [2], 4, 1, 128, 128, 64),
+]
+
+
+def _run_all(wl, q, k, v, m=None):
+    plan = skv.plan_for(wl if m is None else wl.with_workers(m))
+    dev_plan = skv.splitkv_plan_upload(plan)
+    ws = skv.workspace(plan)
+    ws.fill_(float("nan"))
+    skv.splitkv_partial_attn(plan, dev_plan, q, k, v, ws)
+    out_m = torch.full((wl.total_q, wl.num_q_heads, wl.head_dim), float("nan"), device="cuda")
+    lse_m = torch.full((wl.total_q, wl.num_q_heads), float("nan"), device="cuda")
+    skv.splitkv_merge(plan, dev_plan, ws, out_m, lse_m)
+    ws2 = skv.workspace(plan)
+    ws2.fill_(float("nan"))
+    out_f = torch.full_like(out_m, float("nan"))
+    lse_f = torch.full_like(lse_m, float("nan"))
+    skv.splitkv_attn(plan, dev_plan, q, k, v, ws2, out_f, lse_f)
+    torch.cuda.synchronize()
+    return plan, ws, out_m, lse_m, out_f, lse_f
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_small_cases_against_full_oracle(wl):
+    say(f"[gpu] small case {wl.name}")
+    q, k, v = make_qkv(wl, "cuda")
+    plan, ws, out_m, lse_m, out_f, lse_f = _run_all(wl, q, k, v)
+    qh, kh, vh = widen_to_f64(q), widen_to_f64(k), widen_to_f64(v)
+    O, L = attention_ref(qh, kh, vh, wl.kv_lens, wl.q_lens, wl.num_q_heads, wl.num_kv_heads, wl.causal)
+    d_merge = compare(out_m.cpu().numpy(), O, lse_m.cpu().numpy(), L)
+    d_fused = compare(out_f.cpu().numpy(), O, lse_f.cpu().numpy(), L)
+    say(f"  merge: {d_merge}\n  fused: {d_fused}")
+    assert_within(d_merge, wl.dtype, "partial+merge")
+    assert_within(d_fused, wl.dtype, "fused")
+    # The fused call writes single-block sequences directly; all other rows go through
+    # the same merge, so both paths give identical bits.
+    assert torch.equal(out_m, out_f) and torch.equal(lse_m, lse_f)
+    # Every partial against the oracle's per-block partials.
+    parts = partials_ref(qh, kh, vh, wl.kv_lens, wl.q_lens, wl.num_q_heads, wl.num_kv_heads, wl.block_len,
+                         wl.causal)
+    wo, wlse = skv.workspace_views(plan, ws)
+    wo, wlse = wo.cpu().numpy(), wlse.cpu().numpy()
+    assert not np.any(np.isnan(wlse)), "workspace LSE left unwritten"
+    g = wl.group
+    go, gl, ro, rl = [], [], [], []
+    for (s, b, kap), (Ob, Lb) in parts.items():
+        r0 = partial_row(wl, s, b, kap, 0)
+        rows = wl.q_lens[s] * g
+        go.append(wo[r0:r0 + rows])
+        gl.append(wlse[r0:r0 + rows])
+        ro.append(Ob.reshape(rows, wl.head_dim))
+        rl.append(Lb.reshape(rows))
+    d_part = compare(np.concatenate(go), np.concatenate(ro), np.concatenate(gl), np.concatenate(rl))
+    say(f"  partials: {d_part}")
+    assert_within(d_part, wl.dtype, "partials")
+
+
+def test_bitwise_identical_across_worker_counts():
+    wl = SMALL[1]
+    say(f"[gpu] worker-count invariance on {wl.name}")
+    q, k, v = make_qkv(wl, "cuda")
+    ref = None
+    for m in (1, 3, 16, 256):
+        _, _, out_m, lse_m, out_f, lse_f = _run_all(wl, q, k, v, m)
+        if ref is None:
+            ref = (out_f.clone(), lse_f.clone())
+        assert torch.equal(out_f, ref[0]) and torch.equal(lse_f, ref[1]), f"m={m}"
+        assert torch.equal(out_m, ref[0])
+
+
+def test_repeated_calls_reuse_buffers():
+    wl = SMALL[2]
+    say(f"[gpu] repeated calls on {wl.name}")
+    q, k, v = make_qkv(wl, "cuda")
+    plan = skv.plan_for(wl)
+    dev_plan = skv.splitkv_plan_upload(plan)
+    ws = skv.workspace(plan)
+    outs = [skv.splitkv_attn(plan, dev_plan, q, k, v, ws) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+
+
+# --------------------------------------------------------------------------- full sizes
+
+def _sample_pairs(rng, wl, s, count):
+    qs = wl.q_lens[s]
+    pairs = {(qs - 1, int(rng.integers(0, wl.num_q_heads))), (0, int(rng.integers(0, wl.num_q_heads)))}
+    while len(pairs) < min(count, qs * wl.num_q_heads):
+        pairs.add((int(rng.integers(0, qs)), int(rng.integers(0, wl.num_q_heads))))
+    return sorted(pairs)
+
+
+def _check_sampled(wl, seqs, per_seq, seed=0, partial_units=4):
+    say(f"[gpu] full-size {wl.name}: drawing inputs")
+    q, k, v = make_qkv(wl, "cuda")
+    plan = skv.plan_for(wl)
+    dev_plan = skv.splitkv_plan_upload(plan)
+    ws = skv.workspace(plan)
+    out = torch.full((wl.total_q, wl.num_q_heads, wl.head_dim), float("nan"), device="cuda")
+    lse = torch.full((wl.total_q, wl.num_q_heads), float("nan"), device="cuda")
+    say(f"[gpu] full-size {wl.name}: fused call")
+    skv.splitkv_attn(plan, dev_plan, q, k, v, ws, out, lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any() and torch.isfinite(lse).all(), "unwritten or non-finite outputs"
+    say(f"[gpu] full-size {wl.name}: separate calls")
+    ws2 = skv.workspace(plan)
+    skv.splitkv_partial_attn(plan, dev_plan, q, k, v, ws2)
+    out2, lse2 = skv.splitkv_merge(plan, dev_plan, ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    wo, wlse = skv.workspace_views(plan, ws2)
+
+    rng = np.random.default_rng(seed)
+    qo, ko = offsets(wl.q_lens), offsets(wl.kv_lens)
+    g, sc = wl.group, scale_of(wl)
+    got_o, got_l, ref_o, ref_l = [], [], [], []
+    pg_o, pg_l, pr_o, pr_l = [], [], [], []
+    for s in seqs:
+        n, qs = wl.kv_lens[s], wl.q_lens[s]
+        pairs = _sample_pairs(rng, wl, s, per_seq)
+        by_kv = {}
+        for i, h in pairs:
+            by_kv.setdefault(h // g, []).append((i, h))
+        for kap, prs in by_kv.items():
+            Kh = widen_to_f64(k[ko[s]:ko[s + 1], kap])
+            Vh = widen_to_f64(v[ko[s]:ko[s + 1], kap])
+            Qr = np.stack([widen_to_f64(q[qo[s] + i, h]) for i, h in prs])
+            pos = np.array([n - qs + i for i, _ in prs], dtype=np.int64)
+            Oref, Lref = attend_rows(Qr, pos, Kh, Vh, sc, wl.causal)
+            for t, (i, h) in enumerate(prs):
+                got_o.append(out[qo[s] + i, h].cpu().numpy())
+                got_l.append(float(lse[qo[s] + i, h]))
+            ref_o.append(Oref)
+            ref_l.append(Lref)
+            # A few partials of the same rows: first block, last block, one in between.
+            nb = wl.num_blocks(s)
+            for b in sorted({0, nb - 1, int(rng.integers(0, nb))})[:partial_units]:
+                Ob, Lb = attend_rows(Qr, pos, Kh, Vh, sc, wl.causal, b * wl.block_len, (b + 1) * wl.block_len)
+                for t, (i, h) in enumerate(prs):
+                    r = partial_row(wl, s, b, kap, i * g + (h - kap * g))
+                    pg_o.append(wo[r].cpu().numpy())
+                    pg_l.append(float(wlse[r]))
+                pr_o.append(Ob)
+                pr_l.append(Lb)
+    d = compare(np.stack(got_o), np.concatenate(ref_o), np.array(got_l), np.concatenate(ref_l))
+    dp = compare(np.stack(pg_o), np.concatenate(pr_o), np.array(pg_l), np.concatenate(pr_l))
+    say(f"  sampled outputs ({len(got_o)}): {d}\n  sampled partials ({len(pg_o)}): {dp}")
+    assert_within(d, wl.dtype, "sampled outputs")
+    assert_within(dp, wl.dtype, "sampled partials")
+    del q, k, v, ws, ws2
+    torch.cuda.empty_cache()
+
+
+def test_full_small_fp32():
+    wl = get_workload("small")
+    _check_sampled(wl, [0], 4)
+
+
+def test_full_batch8_whole_output():
+    wl = get_workload("batch8")
+    say(f"[gpu] full-size {wl.name}: whole output against the oracle")
+    q, k, v = make_qkv(wl, "cuda")
+    plan = skv.plan_for(wl)
+    dev_plan = skv.splitkv_plan_upload(plan)
+    out, lse = skv.splitkv_attn(plan, dev_plan, q, k, v)
+    torch.cuda.synchronize()
+    O, L = attention_ref(widen_to_f64(q), widen_to_f64(k), widen_to_f64(v), wl.kv_lens, wl.q_lens,
+                         wl.num_q_heads, wl.num_kv_heads, wl.causal)
+    d = compare(out.cpu().numpy(), O, lse.cpu().numpy(), L)
+    say(f"  whole output: {d}")
+    assert_within(d, wl.dtype, "batch8 whole output")
+    _check_sampled(wl, range(8), 6)
+
+
+def test_full_long_context():
+    _check_sampled(get_workload("long"), [0], 24)
+
+
+def test_full_lognormal():
+    wl = get_workload("lognormal")
+    order = np.argsort(wl.kv_lens)
+    seqs = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), int(np.argmax(wl.q_lens)),
+                   int(np.argmin(wl.q_lens))})
+    _check_sampled(wl, seqs, 8)
+
+
+def test_full_mixed():
+    wl = get_workload("mixed")
+    _check_sampled(wl, [0, 1, 77, 127, 128, 131], 8)
+
+
+def test_full_decode_only():
+    wl = get_workload("decode")
+    _check_sampled(wl, [0, 64, 127], 8)

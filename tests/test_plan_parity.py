@@ -1,0 +1,59 @@
+"""The library's C++ LPT planner against the pure-Python oracle, bit for bit (CPU)."""
+
+import numpy as np
+import pytest
+
+from oracle import plan_ref
+from split_kv_exact_amd import splitkv_plan
+from workloads import WORKLOADS, get_workload
+
+
+def compare(kv, q, hq, hkv, b, m, gran=0, d=128):
+    pl = splitkv_plan(kv, q, hq, hkv, d, b, m, True, gran)
+    ex = pl.export()
+    inf = pl.info()
+    ref = plan_ref(kv, q, hq, hkv, b, m, gran)
+    units = ref["units"]
+    assert inf["num_units"] == len(units)
+    assert ex["unit_seq"].tolist() == [u[0] for u in units]
+    assert ex["unit_block"].tolist() == [u[1] for u in units]
+    assert ex["unit_kv_head"].tolist() == [u[2] for u in units]
+    assert ex["unit_len"].tolist() == [u[3] for u in units]
+    assert ex["unit_cost"].tolist() == ref["costs"]
+    assert ex["worker_of"].tolist() == ref["worker_of"]
+    assert ex["worker_ptr"].tolist() == ref["worker_ptr"]
+    assert ex["worker_units"].tolist() == ref["worker_units"]
+    assert ex["load"].tolist() == ref["loads"]
+    assert inf["makespan"] == ref["makespan"]
+    assert inf["total_cost"] == ref["total_cost"]
+    assert inf["imbalance"] == ref["imbalance"]  # the same float64 division, bit for bit
+    costs = ref["costs"]
+    assert inf["lower_bound"] == max(-(-sum(costs) // m), max(costs))
+    return inf
+
+
+@pytest.mark.parametrize("key", sorted(WORKLOADS))
+@pytest.mark.parametrize("gran", [0, 1])
+def test_workload_plans_bit_exact(key, gran):
+    wl = get_workload(key)
+    compare(wl.kv_lens, wl.q_lens, wl.num_q_heads, wl.num_kv_heads, wl.block_len, wl.num_workers, gran,
+            wl.head_dim)
+
+
+def test_random_instances_bit_exact():
+    rng = np.random.default_rng(30)
+    for _ in range(40):
+        S = int(rng.integers(1, 12))
+        hkv = int(rng.integers(1, 5))
+        g = int(rng.integers(1, 5))
+        b = int(rng.choice([1, 3, 16, 100, 512]))
+        m = int(rng.integers(1, 40))
+        kv = [int(x) for x in rng.integers(1, 3000, size=S)]
+        q = [int(rng.integers(1, k + 1)) for k in kv]
+        q = [min(x, 50) for x in q]
+        compare(kv, q, g * hkv, hkv, b, m, int(rng.integers(0, 2)))
+
+
+def test_worker_count_larger_than_units():
+    inf = compare([10], [2], 2, 1, 4, 64)
+    assert inf["makespan"] == inf["lower_bound"]
