@@ -136,6 +136,9 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="skip the cold-cache per-step measurement")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 1 GiB device copy (a kernel of known traffic, for scaling "
+                         "hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -181,6 +184,13 @@ def main() -> int:
     def merge():
         skv.splitkv_merge(plan, dev_plan, ws, out, lse)
 
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
