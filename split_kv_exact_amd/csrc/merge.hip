@@ -4,9 +4,13 @@
 // attention. With block partials (O_b, LSE_b) for b = 0..nb-1 of one query row:
 //   M = max_b LSE_b,  w_b = e^(LSE_b - M),  O = sum_b w_b O_b / sum_b w_b,
 //   LSE = M + ln sum_b w_b,
-// because e^(LSE_b) O_b and e^(LSE_b) are the block's sums of e^s v and e^s. Blocks
-// are summed in block order by every lane, so the result does not depend on how the
-// plan spread the blocks over workers.
+// because e^(LSE_b) O_b and e^(LSE_b) are the block's sums of e^s v and e^s.
+//
+// Layout of the work: lane b holds LSE_b (64 blocks at a time), so M and sum_b w_b are
+// wave reductions; the output row is then accumulated in block order, each lane owning
+// head_dim/64 dimensions, with the loads of 8 blocks issued before they are used. Block
+// order is fixed, so the result does not depend on how the plan spread the blocks
+// over workers.
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
@@ -18,6 +22,18 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.69314718055994531f;
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr int WAVES = 4;
+constexpr int UNROLL = 8;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
@@ -40,23 +56,47 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int kv = int(rem / sq.rows);
   const int r = int(rem - int64_t(kv) * sq.rows);
   const int i = r / a.g, hl = r - i * a.g;
-  const int64_t r0 = sq.row_base + int64_t(kv) * sq.nb * sq.rows + r;  // block b: r0 + b * rows
+  const int nb = sq.nb;
+  const int64_t r0 = sq.row_base + int64_t(kv) * nb * sq.rows + r;  // block b: r0 + b * rows
+  const int64_t rs = sq.rows;
 
+  // M = max_b LSE_b, then W = sum_b e^(LSE_b - M), lanes over blocks.
   float M = NEG_INF;
-  for (int b = 0; b < sq.nb; ++b) M = fmaxf(M, a.ws_lse[r0 + int64_t(b) * sq.rows]);
-  float W = 0.f;
+  for (int b0 = 0; b0 < nb; b0 += 64) {
+    const int b = b0 + lane;
+    M = fmaxf(M, b < nb ? a.ws_lse[r0 + b * rs] : NEG_INF);
+  }
+  M = wave_max(M);
   float o[DPL];
 #pragma unroll
   for (int k = 0; k < DPL; ++k) o[k] = 0.f;
+  float W = 0.f;
   if (M != NEG_INF) {
-    for (int b = 0; b < sq.nb; ++b) {
-      const int64_t rb = r0 + int64_t(b) * sq.rows;
-      const float wb = __builtin_amdgcn_exp2f((a.ws_lse[rb] - M) * LOG2E);
-      W += wb;
-      const float* ob = a.ws_o + rb * D;
+    for (int b0 = 0; b0 < nb; b0 += 64) {
+      const int b = b0 + lane;
+      const float wl = b < nb ? __builtin_amdgcn_exp2f((a.ws_lse[r0 + b * rs] - M) * LOG2E) : 0.f;
+      W += wl;
+      const int cnt = min(64, nb - b0);
+      for (int j0 = 0; j0 < cnt; j0 += UNROLL) {
+        float v[UNROLL][DPL];
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) o[k] = __builtin_fmaf(wb, ob[lane + 64 * k], o[k]);
+        for (int u = 0; u < UNROLL; ++u) {
+          const int jb = min(j0 + u, cnt - 1);
+          const float* ob = a.ws_o + (r0 + (b0 + jb) * rs) * D;
+#pragma unroll
+          for (int k = 0; k < DPL; ++k) v[u][k] = ob[lane + 64 * k];
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          if (j0 + u < cnt) {
+            const float wb = __shfl(wl, j0 + u);
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) o[k] = __builtin_fmaf(wb, v[u][k], o[k]);
+          }
+        }
+      }
     }
+    W = wave_sum(W);
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
   const int64_t idx = (sq.q_base + i) * a.Hq + kv * a.g + hl;

@@ -310,10 +310,13 @@ __device__ __forceinline__ void softmax_step(State<D>& st, int nt, const unsigne
       for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[t][tt][e]);
-      mx = max4(mx);
-      // Move the reference (and rescale) only on a large increase; -inf -> finite always moves.
-      const bool grow = mx * c > st.m[t] * c + RESCALE_LOG2 || (st.m[t] == NEG_INF && mx != NEG_INF);
-      if (__any(grow)) {
+      // Move the reference (and rescale) only on a large increase; -inf -> finite always
+      // moves. The test first uses this lane's own scores: only when some lane would move
+      // is the row max formed across the row's four lanes (rare after the first step).
+      const bool grow_lane = mx * c > st.m[t] * c + RESCALE_LOG2 || (st.m[t] == NEG_INF && mx != NEG_INF);
+      if (__any(grow_lane)) {
+        mx = max4(mx);
+        const bool grow = mx * c > st.m[t] * c + RESCALE_LOG2 || (st.m[t] == NEG_INF && mx != NEG_INF);
         const float mnew = grow ? mx : st.m[t];
         const float alpha = grow ? (st.m[t] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((st.m[t] - mnew) * c)) : 1.f;
         st.m[t] = mnew;
@@ -369,7 +372,8 @@ __device__ __forceinline__ void softmax_step(State<D>& st, int nt, const unsigne
 
 }
 
-// Normalise and store one row tile (row li of the tile, dims 16dt+4G..+3).
+// Normalise and store one row tile of a finished job (row li of the tile, dims
+// 16dt+4G..+3).
 template <int D>
 __device__ __forceinline__ void write_tile(const State<D>& st, int t, const PartialArgs& a, const Job& J, int tile) {
   using C = Cfg<D>;
@@ -396,6 +400,66 @@ __device__ __forceinline__ void write_tile(const State<D>& st, int t, const Part
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) *reinterpret_cast<f32x4*>(op + 16 * dt + 4 * G) = st.o[t][dt] * inv;
   if (G == 0) *lp = lse;
+}
+
+// Finish job J right after its last stage: combine its key slices (Wk > 1) through
+// the LDS slot that stage used, then store every row tile. The slot is next written by
+// DMA only after the following iteration's barrier. (Finishing before that iteration's
+// DMA issue instead delays the pipeline more than the stores cost here.)
+template <int D>
+__device__ __forceinline__ void finish_job(State<D>& st, const PartialArgs& a, const Job& J, unsigned char* slot,
+                                           int wave, float c) {
+  using C = Cfg<D>;
+  const int lane = threadIdx.x & 63;
+  const int rg = wave % J.Wr, ks = wave / J.Wr;
+  const int ntw = ks < J.Wk && J.tile_hi - J.tile_lo - rg > 0 ? (J.tile_hi - J.tile_lo - rg + J.Wr - 1) / J.Wr : 0;
+  const int nt = min(ntw, RTW);
+  if (J.Wk == 1) {
+#pragma unroll
+    for (int t = 0; t < RTW; ++t)
+      if (t < nt) write_tile<D>(st, t, a, J, J.tile_lo + rg + t * J.Wr);
+    return;
+  }
+  // Two key slices per row group; one round per tile index (<= Wr records each). The
+  // loop is unrolled with compile-time tile indices: a runtime index would put the
+  // wave state in scratch memory.
+  float* mbuf = reinterpret_cast<float*>(slot);
+  const int rounds = (J.tile_hi - J.tile_lo + J.Wr - 1) / J.Wr;
+#pragma unroll
+  for (int t = 0; t < RTW; ++t) {
+    if (t >= rounds) break;
+    lds_barrier();  // all waves are done with the slot's tiles / the previous round
+    if (ks == 1 && t < nt) {
+      float* rec = mbuf + rg * C::MSLOT;
+      rec[lane] = st.m[t];
+      rec[64 + lane] = st.l[t];
+      rec[128 + lane] = st.ls[t][0];
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) rec[(3 + dt * 4 + q4) * 64 + lane] = st.o[t][dt][q4];
+    }
+    lds_barrier();
+    if (ks == 0 && t < nt) {
+      const float* rec = mbuf + rg * C::MSLOT;
+      const float m2 = rec[lane];
+      const float ms = fmaxf(st.m[t], m2);
+      if (ms != NEG_INF) {
+        const float a1 = __builtin_amdgcn_exp2f((st.m[t] - ms) * c);
+        const float a2 = __builtin_amdgcn_exp2f((m2 - ms) * c);
+        st.l[t] = st.l[t] * a1 + rec[64 + lane] * a2;
+        const float ls2 = st.ls[t][0] * a1 + rec[128 + lane] * a2;
+        st.ls[t] = f32x4{ls2, ls2, ls2, ls2};
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            st.o[t][dt][q4] = st.o[t][dt][q4] * a1 + rec[(3 + dt * 4 + q4) * 64 + lane] * a2;
+        st.m[t] = ms;
+      }
+      write_tile<D>(st, t, a, J, J.tile_lo + rg + t * J.Wr);
+    }
+  }
 }
 
 template <int D>
@@ -510,55 +574,8 @@ void partial_bf16_kernel(PartialArgs a, const UnitRec* __restrict__ units, const
     if (nt > 0) {
       for (int h = 0; h < tkw; h += 32) softmax_step<D>(st, nt, slot, tok_stage, tok_w + h, need_mask, c);
     }
-
     if (jj + 1 == J.nst) {
-      // Job end: combine the key slices (Wk > 1) through this slot's LDS, then store.
-      if (J.Wk > 1) {
-        // Two key slices per row group; one round per tile index (<= Wr records each).
-        float* mbuf = reinterpret_cast<float*>(slot);
-        const int rounds = (J.tile_hi - J.tile_lo + J.Wr - 1) / J.Wr;
-        // Unrolled with compile-time tile indices: a runtime index would put the wave
-        // state in scratch memory.
-#pragma unroll
-        for (int t = 0; t < RTW; ++t) {
-          if (t >= rounds) break;
-          lds_barrier();  // every wave is done with this slot (tiles or the previous round)
-          if (ks == 1 && t < nt) {
-            float* rec = mbuf + rg * C::MSLOT;
-            rec[lane] = st.m[t];
-            rec[64 + lane] = st.l[t];
-            rec[128 + lane] = st.ls[t][0];
-#pragma unroll
-            for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-              for (int q4 = 0; q4 < 4; ++q4) rec[(3 + dt * 4 + q4) * 64 + lane] = st.o[t][dt][q4];
-          }
-          lds_barrier();
-          if (ks == 0 && t < nt) {
-            const float* rec = mbuf + rg * C::MSLOT;
-            const float m2 = rec[lane];
-            const float ms = fmaxf(st.m[t], m2);
-            if (ms != NEG_INF) {
-              const float a1 = __builtin_amdgcn_exp2f((st.m[t] - ms) * c);
-              const float a2 = __builtin_amdgcn_exp2f((m2 - ms) * c);
-              st.l[t] = st.l[t] * a1 + rec[64 + lane] * a2;
-              const float ls2 = st.ls[t][0] * a1 + rec[128 + lane] * a2;
-              st.ls[t] = f32x4{ls2, ls2, ls2, ls2};
-#pragma unroll
-              for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                  st.o[t][dt][q4] = st.o[t][dt][q4] * a1 + rec[(3 + dt * 4 + q4) * 64 + lane] * a2;
-              st.m[t] = ms;
-            }
-            write_tile<D>(st, t, a, J, J.tile_lo + rg + t * J.Wr);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int t = 0; t < RTW; ++t)
-          if (t < nt) write_tile<D>(st, t, a, J, J.tile_lo + rg + t * J.Wr);
-      }
+      finish_job<D>(st, a, J, slot, wave, c);
       jj = 0;
       if (!next_job(P, J, u_end)) break;
       describe(a, P, J);
