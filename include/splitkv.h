@@ -102,7 +102,8 @@ typedef struct {
 
 /* Device inputs. Pointers are device memory, caller-owned, read only. Strides are in
  * elements; the innermost (head_dim) stride is 1. Base pointers must be 16-byte
- * aligned and strides multiples of 16 bytes' worth of elements. */
+ * aligned and strides multiples of 16 bytes' worth of elements; with bf16 inputs
+ * every stride must also be at most 2^24 elements (UNSUPPORTED otherwise). */
 typedef struct {
   const void *q, *k, *v;
   int64_t q_stride_tok, q_stride_head;
@@ -152,7 +153,8 @@ void splitkv_plan_destroy(splitkv_plan_t *plan);
  * list. Writes the whole workspace (layout above); every row is written, rows that
  * see no key of a block get O = 0 and LSE = -inf.
  * Errors: INVALID_ARG (null/misaligned pointers, strides), UNSUPPORTED (no kernel for
- * dtype/head_dim), WORKSPACE (ws_bytes < workspace_bytes), HIP (launch failed). */
+ * dtype/head_dim, bf16 stride above 2^24), WORKSPACE (ws_bytes < workspace_bytes),
+ * HIP (launch failed). */
 int splitkv_partial_attn(const splitkv_plan_t *plan, const void *dev_plan, const splitkv_inputs *in,
                          float *ws, size_t ws_bytes, void *hip_stream);
 

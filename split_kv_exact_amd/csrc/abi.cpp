@@ -46,6 +46,12 @@ int check_inputs(const splitkv_plan_t* pl, const splitkv_inputs* in, float* scal
   for (int64_t x : st)
     if (x < 0 || x % vec != 0)
       return fail(SPLITKV_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
+  // The bf16 kernel addresses a lane's rows within one stage or Q tile with 32-bit
+  // byte offsets.
+  if (in->dtype == SPLITKV_BF16)
+    for (int64_t x : st)
+      if (x > (int64_t(1) << 24))
+        return fail(SPLITKV_ERR_UNSUPPORTED, "bf16 strides must be at most 2^24 elements");
   if (!(std::isfinite(in->scale)) || in->scale < 0.f)
     return fail(SPLITKV_ERR_INVALID_ARG, "scale must be finite and >= 0 (0 selects 1/sqrt(head_dim))");
   *scale_out = in->scale == 0.f ? float(1.0 / std::sqrt(double(pl->D))) : in->scale;
@@ -85,6 +91,8 @@ splitkv::PartialArgs partial_args(const splitkv_plan_t* pl, const void* dev_plan
   a.seqs = reinterpret_cast<const splitkv::SeqRec*>(base + pl->layout.seqs);
   a.units = reinterpret_cast<const splitkv::UnitRec*>(base + pl->layout.units);
   a.worker_ptr = reinterpret_cast<const int32_t*>(base + pl->layout.worker_ptr);
+  a.jobs = reinterpret_cast<const splitkv::JobRec*>(base + pl->layout.jobs);
+  a.job_ptr = reinterpret_cast<const int32_t*>(base + pl->layout.job_ptr);
   a.num_workers = pl->m;
   a.Hq = pl->Hq;
   a.Hkv = pl->Hkv;

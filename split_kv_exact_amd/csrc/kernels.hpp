@@ -17,6 +17,8 @@ struct PartialArgs {
   const SeqRec* seqs;
   const UnitRec* units;
   const int32_t* worker_ptr;
+  const JobRec* jobs;       // bf16 kernel: jobs grouped by worker
+  const int32_t* job_ptr;   // bf16 kernel: worker w owns jobs [job_ptr[w], job_ptr[w+1])
   int32_t num_workers;
   int32_t Hq, Hkv, g, B, causal;
   float* ws_o;    // partial outputs [partial_rows, D]

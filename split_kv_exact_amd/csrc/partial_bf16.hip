@@ -1,4 +1,4 @@
-// Partial attention of split-KV units on gfx950 matrix cores (bf16 inputs, fp32 math).
+// Partial attention of split-KV jobs on gfx950 matrix cores (bf16 inputs, fp32 math).
 //
 // Split-KV page, lede: each context KV block yields a result the size of the
 // queries; here that is, for every query row of a unit, the block's softmax output
@@ -6,24 +6,31 @@
 // a CDNA4 design.
 //
 // Execution model
-//   * One workgroup (4 wavefronts, one per SIMD) per LPT worker, one worker per CU
-//     (the LDS footprint admits one workgroup per CU). The workgroup walks its unit
-//     list in plan order as a flat sequence of "jobs" (unit x KV head x row pass),
-//     each cut into stages of 64 keys.
+//   * One workgroup of 8 wavefronts (two per SIMD) per LPT worker, one worker per CU
+//     (the LDS footprint admits one workgroup per CU). The planner cuts every unit
+//     of the worker into jobs (KV head x pass over at most 256 query rows), and the
+//     workgroup walks that job list, each job cut into stages of 64 keys.
 //   * A 3-slot LDS pipeline holds stages: each slot has a K tile, a V tile and (for
-//     units with at most 64 query rows) the unit's Q tile. Slots are filled by
-//     direct global->LDS DMA (global_load_lds_dwordx4, 16 bytes per lane), issued two
-//     stages ahead of the stage being computed and continuing across unit
-//     boundaries, so about 64 KiB per CU stay in flight without staging registers.
-//     Each stage costs one workgroup barrier; completion of a stage's DMA is tracked
-//     with explicit vmcnt waits (loads complete in issue order).
+//     jobs with at most 64 query rows) the job's Q tile. Slots are filled by direct
+//     global->LDS DMA (global_load_lds_dwordx4, 16 bytes per lane), issued two stages
+//     ahead of the stage being computed and continuing across job boundaries, so
+//     about 64 KiB per CU stay in flight without staging registers. A lane's part of
+//     a stage sits at a fixed offset from the stage's base address, so issuing a
+//     stage costs one scalar add per tensor; only a block's last, partial stage
+//     computes clamped offsets.
+//   * Each stage costs one workgroup barrier. Completion of a stage's DMA is tracked
+//     with explicit vmcnt waits: vector-memory instructions complete in issue order,
+//     and the kernel counts every one it issues after a stage (the next stage's DMA
+//     and the result stores, whose number per finished job is fixed), so a wait never
+//     drains more than the stage it needs.
 //   * Tiles are stored row-major (one key per 2*D-byte row) with an XOR swizzle of the
 //     16-byte chunks, chosen so that both read patterns below are free of LDS bank
-//     conflicts.
+//     conflicts and so that a lane's read offsets do not depend on the stage.
 //   * Query rows of a KV head are r = i*g + (h - kv*g) (query token i, head h), in
-//     16-row tiles. With >= 4 tiles the 4 waves split the tiles (up to 4 per wave per
-//     pass, so 256 rows per pass); with fewer tiles the waves also split each stage's
-//     keys two ways and merge their results in LDS at the end of the job.
+//     16-row tiles. With >= 8 tiles the 8 waves split the tiles (up to 2 each, so 256
+//     rows per pass); with fewer tiles the waves also split each stage's keys two ways
+//     and merge their results in LDS at the end of the job. Rows past the last query
+//     row repeat the last row, so every wave stores whole tiles.
 //   * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16, A = 16
 //     keys x 32 dims from the K tile, B = 32 dims x 16 rows of Q in registers). A lane
 //     then owns one query row and 4 keys per 16-key tile: the row max needs two
@@ -47,19 +54,19 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) const bf16x8* lds_bf16x8;
 
-constexpr int NW = 8;          // wavefronts per workgroup (two per SIMD)
-constexpr int TK = 64;         // keys per pipeline stage
-constexpr int NST = 3;         // pipeline slots
-constexpr int RTW = 2;         // row tiles per wave per pass
-constexpr int QLDS_ROWS = 64;  // units with at most this many rows get Q through LDS
+constexpr int NW = 8;           // wavefronts per workgroup (two per SIMD)
+constexpr int TK = kStageKeys;  // keys per pipeline stage
+constexpr int NST = 3;          // pipeline slots
+constexpr int RTW = 2;          // row tiles per wave per pass
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.69314718055994531f;
 constexpr float NEG_INF = -__builtin_huge_valf();
+static_assert(kPassTiles == NW * RTW, "a pass gives every wave up to RTW row tiles");
+static_assert(TK == 64, "a wave's key slice is one or two 32-key steps");
 
 template <int D>
 struct Cfg {
@@ -69,82 +76,104 @@ struct Cfg {
   static constexpr int CH = ROWB / 16;               // 16-byte chunks per row
   static constexpr int RPI = 1024 / ROWB;            // rows per 1 KiB DMA instruction
   static constexpr int TILEB = TK * ROWB;            // bytes of a K or V tile
-  static constexpr int QTILEB = QLDS_ROWS * ROWB;    // bytes of a Q tile
+  static constexpr int QTILEB = kQTileRows * ROWB;   // bytes of a Q tile
   static constexpr int SLOTB = 2 * TILEB + QTILEB;   // bytes per pipeline slot
   static constexpr int KV_INST = TILEB / 1024 / NW;  // DMA instructions per wave per K (or V) tile
   static constexpr int Q_INST = QTILEB / 1024 / NW;  // DMA instructions per wave per Q tile
   static constexpr int MSLOT = 64 * (DT * 4 + 3);    // floats of one merge record (m, l, ls, O)
+  static constexpr int STORES = DT + 1;              // store instructions per finished row tile
   // At least 96 KiB so that a compute unit holds a single workgroup.
   static constexpr int LDSB = NST * SLOTB > 96 * 1024 ? NST * SLOTB : 96 * 1024;
   static_assert(4 * MSLOT * 4 <= SLOTB, "a merge round's records fit in one slot");
   static_assert(KV_INST >= 1 && Q_INST >= 1, "tile sizes");
+  static_assert(CH <= 16 && 32 % CH == 0, "swizzles repeat every 16 rows");
 };
 
 // XOR swizzles of the 16-byte chunk index within a row: conflict-free 16-lane row
-// reads (K, Q) and 32-lane transposing reads (V).
+// reads (K, Q) and 32-lane transposing reads (V). Both depend on the row modulo 16
+// only, and tiles start at multiples of 16 rows.
 template <int D>
 __device__ __forceinline__ int swz_k(int row, int c) { return c ^ (row & (Cfg<D>::CH - 1)); }
 template <int D>
 __device__ __forceinline__ int swz_v(int row, int c) { return c ^ ((2 * row) & (Cfg<D>::CH - 1)); }
 
-// Wait until at most n vector-memory operations of this wave are outstanding, then
+// Wait until at most n vector-memory instructions of this wave are outstanding, then
 // barrier the workgroup (no fence: the pipeline's later DMA must stay in flight).
+// Values past the table wait for everything, which is always safe.
 __device__ __forceinline__ void wait_vm_barrier(int n) {
   switch (n) {
 #define SKV_CASE(N) \
   case N: asm volatile("s_waitcnt vmcnt(" #N ")\n\ts_barrier" ::: "memory"); break;
     SKV_CASE(0) SKV_CASE(1) SKV_CASE(2) SKV_CASE(3) SKV_CASE(4) SKV_CASE(5) SKV_CASE(6) SKV_CASE(7)
-    SKV_CASE(8) SKV_CASE(9) SKV_CASE(10) SKV_CASE(11) SKV_CASE(12)
+    SKV_CASE(8) SKV_CASE(9) SKV_CASE(10) SKV_CASE(11) SKV_CASE(12) SKV_CASE(13) SKV_CASE(14) SKV_CASE(15)
+    SKV_CASE(16) SKV_CASE(17) SKV_CASE(18) SKV_CASE(19) SKV_CASE(20) SKV_CASE(21) SKV_CASE(22) SKV_CASE(23)
+    SKV_CASE(24) SKV_CASE(25) SKV_CASE(26) SKV_CASE(27) SKV_CASE(28) SKV_CASE(29) SKV_CASE(30) SKV_CASE(31)
+    SKV_CASE(32) SKV_CASE(33) SKV_CASE(34) SKV_CASE(35) SKV_CASE(36) SKV_CASE(37) SKV_CASE(38) SKV_CASE(39)
+    SKV_CASE(40) SKV_CASE(41) SKV_CASE(42) SKV_CASE(43) SKV_CASE(44) SKV_CASE(45) SKV_CASE(46) SKV_CASE(47)
 #undef SKV_CASE
     default: asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); break;
   }
+}
+
+// The same, with the two counts of the steady state (a stage's DMA with and without
+// a Q tile) tested first.
+template <int D>
+__device__ __forceinline__ void wait_stage(int n) {
+  constexpr int NKV = 2 * Cfg<D>::KV_INST, NQ = Cfg<D>::Q_INST;
+  if (n == NKV)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(NKV) : "memory");
+  else if (n == NKV + NQ)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(NKV + NQ) : "memory");
+  else {
+    asm volatile("" : "+s"(n));  // keeps the tests above out of the switch below
+    wait_vm_barrier(n);
+  }
+}
+
+// LDS writes and reads of this wave done, then barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ unsigned lds_addr(const unsigned char* p) {
+  typedef __attribute__((address_space(3))) const unsigned char* lds_cptr;
+  return (unsigned)(uintptr_t)(lds_cptr)p;  // 32-bit LDS offset
 }
 
 // Transposing LDS reads (ds_read_b64_tr_b16) issued from inline assembly. Through the
 // builtin, the compiler cannot tell that they read a different pipeline slot than the
 // in-flight DMA writes, and it drains all of that DMA first. The reads and their
 // lgkmcnt wait sit in one asm statement, so no instruction can touch the destination
-// registers while the loads are still in flight.
-__device__ __forceinline__ unsigned lds_addr(const unsigned char* p) {
-  typedef __attribute__((address_space(3))) const unsigned char* lds_cptr;
-  return (unsigned)(uintptr_t)(lds_cptr)p;  // 32-bit LDS offset
+// registers while the loads are still in flight. Lane addresses are a[dt] + OFF (keys
+// 0-15 of the step) and a[dt] + OFF + HI (keys 16-31).
+template <int OFF, int HI>
+__device__ __forceinline__ void tr_read(i16x4 (&lo)[8], i16x4 (&hi)[8], const unsigned (&a)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:%24\n\tds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %2, %18 offset:%24\n\tds_read_b64_tr_b16 %3, %19 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %4, %20 offset:%24\n\tds_read_b64_tr_b16 %5, %21 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %6, %22 offset:%24\n\tds_read_b64_tr_b16 %7, %23 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:%25\n\tds_read_b64_tr_b16 %9, %17 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %10, %18 offset:%25\n\tds_read_b64_tr_b16 %11, %19 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %12, %20 offset:%25\n\tds_read_b64_tr_b16 %13, %21 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %14, %22 offset:%25\n\tds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(lo[4]), "=&v"(lo[5]), "=&v"(lo[6]),
+        "=&v"(lo[7]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]), "=&v"(hi[3]), "=&v"(hi[4]), "=&v"(hi[5]),
+        "=&v"(hi[6]), "=&v"(hi[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF),
+        "i"(OFF + HI));
 }
-
-template <int N>
-__device__ __forceinline__ void tr_read_all(i16x4 (&lo)[N], i16x4 (&hi)[N], const unsigned (&alo)[N],
-                                            const unsigned (&ahi)[N]) {
-  if constexpr (N == 8) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %16\n\tds_read_b64_tr_b16 %1, %17\n\t"
-        "ds_read_b64_tr_b16 %2, %18\n\tds_read_b64_tr_b16 %3, %19\n\t"
-        "ds_read_b64_tr_b16 %4, %20\n\tds_read_b64_tr_b16 %5, %21\n\t"
-        "ds_read_b64_tr_b16 %6, %22\n\tds_read_b64_tr_b16 %7, %23\n\t"
-        "ds_read_b64_tr_b16 %8, %24\n\tds_read_b64_tr_b16 %9, %25\n\t"
-        "ds_read_b64_tr_b16 %10, %26\n\tds_read_b64_tr_b16 %11, %27\n\t"
-        "ds_read_b64_tr_b16 %12, %28\n\tds_read_b64_tr_b16 %13, %29\n\t"
-        "ds_read_b64_tr_b16 %14, %30\n\tds_read_b64_tr_b16 %15, %31\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(lo[4]), "=&v"(lo[5]), "=&v"(lo[6]),
-          "=&v"(lo[7]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]), "=&v"(hi[3]), "=&v"(hi[4]), "=&v"(hi[5]),
-          "=&v"(hi[6]), "=&v"(hi[7])
-        : "v"(alo[0]), "v"(alo[1]), "v"(alo[2]), "v"(alo[3]), "v"(alo[4]), "v"(alo[5]), "v"(alo[6]), "v"(alo[7]),
-          "v"(ahi[0]), "v"(ahi[1]), "v"(ahi[2]), "v"(ahi[3]), "v"(ahi[4]), "v"(ahi[5]), "v"(ahi[6]), "v"(ahi[7]));
-  } else {
-    static_assert(N == 4, "head_dim 64 or 128");
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %9\n\t"
-        "ds_read_b64_tr_b16 %2, %10\n\tds_read_b64_tr_b16 %3, %11\n\t"
-        "ds_read_b64_tr_b16 %4, %12\n\tds_read_b64_tr_b16 %5, %13\n\t"
-        "ds_read_b64_tr_b16 %6, %14\n\tds_read_b64_tr_b16 %7, %15\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]),
-          "=&v"(hi[3])
-        : "v"(alo[0]), "v"(alo[1]), "v"(alo[2]), "v"(alo[3]), "v"(ahi[0]), "v"(ahi[1]), "v"(ahi[2]), "v"(ahi[3]));
-  }
+template <int OFF, int HI>
+__device__ __forceinline__ void tr_read(i16x4 (&lo)[4], i16x4 (&hi)[4], const unsigned (&a)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\tds_read_b64_tr_b16 %1, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %2, %10 offset:%12\n\tds_read_b64_tr_b16 %3, %11 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:%13\n\tds_read_b64_tr_b16 %5, %9 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %6, %10 offset:%13\n\tds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]),
+        "=&v"(hi[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF), "i"(OFF + HI));
 }
-
-// LDS writes and reads of this wave done, then barrier.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ float max4(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
@@ -155,134 +184,180 @@ __device__ __forceinline__ float sum4(float x) {
   return x + __shfl_xor(x, 32);
 }
 
-// Read-only plan records. Passed as separate __restrict__ kernel arguments so the
-// compiler can prove no store of the kernel aliases them and read them with scalar
-// loads: a vector load here would be counted by vmcnt behind the in-flight DMA and
-// waiting for it would drain the whole pipeline.
-struct Plan {
-  const UnitRec* __restrict__ units;
-  const SeqRec* __restrict__ seqs;
-};
-
-// One job: (unit, KV head, row pass) and everything derived from it.
-struct Job {
-  int ui, kv, pass;
-  int block, len, lim0, R, nrt, Wr, Wk, npass, tile_lo, tile_hi, nst;
-  bool qlds, direct;
-  SeqRec sq;
-};
-
-__device__ __forceinline__ void describe(const PartialArgs& a, const Plan& P, Job& J) {
-  const UnitRec u = P.units[J.ui];
-  J.sq = P.seqs[u.seq];
-  J.block = u.block;
-  const int64_t key0 = int64_t(u.block) * a.B;
-  J.len = int(min(int64_t(a.B), J.sq.n - key0));
-  // Row r (query token i = r / g) sees block keys t <= lim0 + i; lim0 >= 1 - q.
-  J.lim0 = int(min(int64_t(J.len), J.sq.n - J.sq.q - key0));
-  J.R = J.sq.rows;
-  J.nrt = (J.R + 15) >> 4;
-  // Waves split the row tiles Wr ways and each stage's keys Wk ways (Wr * Wk <= NW;
-  // the other waves only load). With >= 8 tiles: up to 16 tiles (256 rows) per pass.
-  J.Wr = J.nrt >= 8 ? 8 : (J.nrt >= 4 ? 4 : (J.nrt >= 2 ? 2 : 1));
-  J.Wk = J.Wr == 8 ? 1 : 2;
-  J.npass = J.Wr == 8 ? (J.nrt + NW * RTW - 1) / (NW * RTW) : 1;
-  J.tile_lo = J.Wr == 8 ? J.pass * NW * RTW : 0;
-  J.tile_hi = min(J.nrt, J.tile_lo + (J.Wr == 8 ? NW * RTW : J.nrt));
-  const int rmax = min(J.R, J.tile_hi * 16) - 1;
-  const int tmax = a.causal ? min(J.len - 1, J.lim0 + rmax / a.g) : J.len - 1;
-  J.nst = tmax < 0 ? 1 : (tmax + TK) / TK;
-  J.qlds = J.R <= QLDS_ROWS;
-  J.direct = a.out != nullptr && J.sq.nb == 1;
-}
-
-// Advance to the next job of the worker; returns false when the list is exhausted.
-__device__ __forceinline__ bool next_job(const Plan& P, Job& J, int u_end) {
-  if (++J.pass < J.npass) return true;
-  J.pass = 0;
-  const UnitRec u = P.units[J.ui];
-  if (++J.kv < u.kv0 + u.nkv) return true;
-  if (++J.ui >= u_end) return false;
-  J.kv = P.units[J.ui].kv0;
-  return true;
-}
-
-// Issue the DMA of stage j of job J into one pipeline slot; returns the number of
-// vector-memory instructions this wave issued.
+// Per-lane constant offsets.
 template <int D>
-__device__ __forceinline__ int issue_stage(const PartialArgs& a, const Job& J, int j, unsigned char* slot, int wave,
-                                           int lane) {
+struct LaneOff {
+  uint32_t dk[Cfg<D>::KV_INST];  // DMA: this lane's 16 bytes of a full K stage, from the stage base
+  uint32_t dv[Cfg<D>::KV_INST];  // the same for V
+  uint32_t kr[Cfg<D>::DC];       // LDS: K operand (key row li, dims 32dc + 8G..+7) in a 16-key tile
+  uint32_t vr[Cfg<D>::DT];       // LDS: V^T operand (key row 4G + li/4, dims 16dt + 4(li%4)..+3)
+};
+
+template <int D>
+__device__ __forceinline__ void lane_offsets(LaneOff<D>& lo, int wave, int lane, uint32_t kst, uint32_t vst) {
   using C = Cfg<D>;
+  const int G = lane >> 4, li = lane & 15;
   const int cs = lane % C::CH;
-  const int64_t kv0 = (J.sq.kv_base + int64_t(J.block) * a.B);
-  const __bf16* kb = reinterpret_cast<const __bf16*>(a.k) + kv0 * a.k_st + int64_t(J.kv) * a.k_sh;
-  const __bf16* vb = reinterpret_cast<const __bf16*>(a.v) + kv0 * a.v_st + int64_t(J.kv) * a.v_sh;
 #pragma unroll
   for (int in = 0; in < C::KV_INST; ++in) {
-    const int gi = wave * C::KV_INST + in;
-    const int row = gi * C::RPI + lane / C::CH;
-    // Keys past the block end re-read the last key: finite data, masked out later.
-    const int tok = min(j * TK + row, J.len - 1);
-    const __bf16* ks = kb + int64_t(tok) * a.k_st + 8 * swz_k<D>(row, cs);
-    const __bf16* vs = vb + int64_t(tok) * a.v_st + 8 * swz_v<D>(row, cs);
-    __builtin_amdgcn_global_load_lds(ks, (lds_void*)(slot + gi * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vs, (lds_void*)(slot + C::TILEB + gi * 1024), 16, 0, 0);
+    const int row = (wave * C::KV_INST + in) * C::RPI + lane / C::CH;
+    lo.dk[in] = uint32_t(row) * kst + 16u * swz_k<D>(row, cs);
+    lo.dv[in] = uint32_t(row) * vst + 16u * swz_v<D>(row, cs);
+  }
+#pragma unroll
+  for (int dc = 0; dc < C::DC; ++dc) lo.kr[dc] = li * C::ROWB + 16 * swz_k<D>(li, 4 * dc + G);
+  const int e = li >> 2, cc = li & 3, r = 4 * G + e;
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) lo.vr[dt] = r * C::ROWB + 16 * swz_v<D>(r, 2 * dt + (cc >> 1)) + 8 * (cc & 1);
+}
+
+// The DMA side of the pipeline: the job and stage to issue next.
+struct Loader {
+  int job, end;  // job being loaded; end of the worker's job list
+  int stage;     // next stage of that job
+  int nst, len, flags;
+  const unsigned char* kb;  // K / V address of the next stage's first key, this job's KV head
+  const unsigned char* vb;
+};
+
+__device__ __forceinline__ void open_job(Loader& L, const PartialArgs& a, const JobRec* __restrict__ jobs) {
+  const JobRec j = jobs[L.job];
+  L.stage = 0;
+  L.nst = j.nst;
+  L.len = j.len;
+  L.flags = j.flags;
+  L.kb = reinterpret_cast<const unsigned char*>(a.k) + 2 * (j.kv_tok * a.k_st + int64_t(j.kv) * a.k_sh);
+  L.vb = reinterpret_cast<const unsigned char*>(a.v) + 2 * (j.kv_tok * a.v_st + int64_t(j.kv) * a.v_sh);
+}
+
+// Issue the DMA of the loader's next stage into one pipeline slot and advance the
+// loader; returns the number of vector-memory instructions this wave issued.
+template <int D>
+__device__ __forceinline__ int issue_stage(const PartialArgs& a, const JobRec* __restrict__ jobs, Loader& L,
+                                           unsigned char* slot, const LaneOff<D>& lo, int wave, int lane,
+                                           uint32_t kst, uint32_t vst) {
+  using C = Cfg<D>;
+  const int rem = L.len - L.stage * TK;  // keys of the block from this stage's first key on
+  if (rem >= TK) {
+#pragma unroll
+    for (int in = 0; in < C::KV_INST; ++in) {
+      const int gi = wave * C::KV_INST + in;
+      __builtin_amdgcn_global_load_lds(L.kb + lo.dk[in], (lds_void*)(slot + gi * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(L.vb + lo.dv[in], (lds_void*)(slot + C::TILEB + gi * 1024), 16, 0, 0);
+    }
+  } else {
+    // The block ends inside this stage: rows past its end re-read its last key (finite
+    // data, masked out later).
+    const int cs = lane % C::CH;
+#pragma unroll
+    for (int in = 0; in < C::KV_INST; ++in) {
+      const int gi = wave * C::KV_INST + in;
+      const int row = gi * C::RPI + lane / C::CH;
+      const uint32_t t = uint32_t(min(row, rem - 1));
+      __builtin_amdgcn_global_load_lds(L.kb + (t * kst + 16u * swz_k<D>(row, cs)), (lds_void*)(slot + gi * 1024),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(L.vb + (t * vst + 16u * swz_v<D>(row, cs)),
+                                       (lds_void*)(slot + C::TILEB + gi * 1024), 16, 0, 0);
+    }
   }
   int n = 2 * C::KV_INST;
-  if (J.qlds && j == 0) {
-    const __bf16* qb = reinterpret_cast<const __bf16*>(a.q);
+  if (L.stage == 0 && (L.flags & kJobQTile)) {
+    // The job's query rows (at most 64) ride with its first stage; rows past the last
+    // one repeat it.
+    const JobRec j = jobs[L.job];
+    const unsigned char* qb =
+        reinterpret_cast<const unsigned char*>(a.q) + 2 * (j.q_tok * a.q_st + int64_t(j.kv) * a.g * a.q_sh);
+    const uint32_t qst = uint32_t(a.q_st) * 2, qsh = uint32_t(a.q_sh) * 2;
+    const int cs = lane % C::CH;
 #pragma unroll
     for (int in = 0; in < C::Q_INST; ++in) {
       const int gi = wave * C::Q_INST + in;
       const int row = gi * C::RPI + lane / C::CH;
-      const int rr = min(row, J.R - 1);  // padding rows repeat the last row
+      const int rr = min(row, j.rows - 1);
       const int i = rr / a.g, hl = rr - i * a.g;
-      const __bf16* qs = qb + (J.sq.q_base + i) * a.q_st + int64_t(J.kv * a.g + hl) * a.q_sh + 8 * swz_k<D>(row, cs);
-      __builtin_amdgcn_global_load_lds(qs, (lds_void*)(slot + 2 * C::TILEB + gi * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(qb + (uint32_t(i) * qst + uint32_t(hl) * qsh + 16u * swz_k<D>(row, cs)),
+                                       (lds_void*)(slot + 2 * C::TILEB + gi * 1024), 16, 0, 0);
     }
     n += C::Q_INST;
   }
+  ++L.stage;
+  L.kb += TK * kst;
+  L.vb += TK * vst;
   return n;
+}
+
+// The compute side: the job being computed and this wave's share of it.
+struct Work {
+  int job, jj;  // job index; stage within the job
+  JobRec j;
+  int wr_log, Wk;        // row groups 2^wr_log, key slices Wk
+  int rg, ks, nt;        // this wave's row group, key slice, row tiles (<= RTW)
+  int tkw, tok_w;        // keys per stage of this wave's slice, and its first key in the stage
+  int min_lim, max_lim;  // last visible block key of this wave's first / last row
+};
+
+// Query row of tile `tile`, lane row li, with rows past the last repeating it.
+__device__ __forceinline__ int tile_row(const JobRec& j, int tile, int li) { return min(tile * 16 + li, j.rows - 1); }
+
+// Load job w.job and derive this wave's share.
+__device__ __forceinline__ void open_work(Work& w, const JobRec* __restrict__ jobs, int wave, int g) {
+  w.j = jobs[w.job];
+  w.jj = 0;
+  // Waves split the row tiles 2^wr_log ways and each stage's keys Wk ways
+  // (2^wr_log * Wk <= NW; the other waves only load).
+  w.wr_log = w.j.flags & kJobWrMask;
+  w.Wk = w.wr_log == 3 ? 1 : 2;
+  const int Wr = 1 << w.wr_log;
+  w.rg = wave & (Wr - 1);
+  w.ks = wave >> w.wr_log;
+  const int ntw = w.ks < w.Wk ? (w.j.tile_n - w.rg + Wr - 1) >> w.wr_log : 0;
+  w.nt = min(max(ntw, 0), RTW);
+  w.tkw = TK / w.Wk;
+  w.tok_w = w.ks * w.tkw;
+  const int first = tile_row(w.j, w.j.tile_lo + w.rg, 0);
+  const int last = tile_row(w.j, w.j.tile_lo + w.rg + max(w.nt - 1, 0) * Wr, 15);
+  w.min_lim = min(w.j.lim0 + first / g, w.j.len - 1);
+  w.max_lim = min(w.j.lim0 + last / g, w.j.len - 1);
 }
 
 template <int D>
 struct State {
   f32x4 o[RTW][Cfg<D>::DT];
   bf16x8 q[RTW][Cfg<D>::DC];
-  f32x4 ls[RTW];  // sum of the bf16-rounded p of this lane's row (every entry equal)
-  float m[RTW];   // running reference max of raw scores (row of this lane)
-  float l[RTW];   // this lane's share of the row sum of the fp32 p
-  int lim[RTW];  // last visible block key of this lane's row
+  f32x4 ls[RTW];   // sum of the bf16-rounded p of this lane's row (every entry equal)
+  float m[RTW];    // running reference max of raw scores (row of this lane)
+  float thr[RTW];  // scores above this move the reference: m + RESCALE_LOG2 / c
+  float nmc[RTW];  // -m * c (0 while m = -inf)
+  float l[RTW];    // this lane's share of the row sum of the fp32 p
+  int lim[RTW];    // last visible block key of this lane's row
 };
 
-// One online-softmax step for this wave: its nt row tiles against 32 keys of the
-// stage (two 16-key tiles) starting at key `tok` of the stage.
-//
 // The running reference max m moves only when a row's max exceeds it by more than
 // RESCALE_LOG2 in base 2 (then O and l are rescaled); otherwise p = 2^(s*c - m*c) may
 // reach 2^RESCALE_LOG2, which fp32 and bf16 hold exactly in range. O, l and LSE all use
 // the same reference, so the result does not depend on when it moved.
 constexpr float RESCALE_LOG2 = 8.f;
 
-template <int D>
-__device__ __forceinline__ void softmax_step(State<D>& st, int nt, const unsigned char* slot, int tok_stage, int tok,
-                                             bool need_mask, float c) {
+// One online-softmax step for this wave: its nt row tiles against 32 keys, block keys
+// key0.. . ka / va are the stage's K / V operand addresses of the wave's first key;
+// the step's keys start KOFF rows later.
+template <int D, int KOFF>
+__device__ __forceinline__ void softmax_step(State<D>& st, int nt, const unsigned (&ka)[Cfg<D>::DC],
+                                             const unsigned (&va)[Cfg<D>::DT], int key0, bool need_mask, float c,
+                                             float inv_c) {
   using C = Cfg<D>;
   const int lane = threadIdx.x & 63;
-  const int G = lane >> 4, li = lane & 15;
-  const unsigned char* kt = slot;
-  const unsigned char* vt = slot + C::TILEB;
+  const int G = lane >> 4;
 
   // S^T = K Q^T for each 16-key tile, shared K operands across the row tiles.
   constexpr int NT = 2;
   f32x4 s[RTW][NT];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
-    const int row = tok + 16 * tt + li;
     bf16x8 kop[C::DC];
 #pragma unroll
     for (int dc = 0; dc < C::DC; ++dc)
-      kop[dc] = *reinterpret_cast<const bf16x8*>(kt + row * C::ROWB + 16 * swz_k<D>(row, 4 * dc + G));
+      kop[dc] = *reinterpret_cast<lds_bf16x8>(uintptr_t(ka[dc] + (KOFF + 16 * tt) * C::ROWB));
 #pragma unroll
     for (int t = 0; t < RTW; ++t) {
       if (t < nt) {
@@ -299,57 +374,46 @@ __device__ __forceinline__ void softmax_step(State<D>& st, int nt, const unsigne
   for (int t = 0; t < RTW; ++t) {
     if (t < nt) {
       if (need_mask) {
+        // Entry e of tile tt is block key key0 + 16tt + 4G + e.
+        const int d = st.lim[t] - (key0 + 4 * G);
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (tok_stage + tok + 16 * tt + 4 * G + e > st.lim[t]) s[t][tt][e] = NEG_INF;
+            if (16 * tt + e > d) s[t][tt][e] = NEG_INF;
       }
-      float mx = s[t][0][0];
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[t][tt][e]);
+      float mx = fmaxf(fmaxf(s[t][0][0], s[t][0][1]), fmaxf(s[t][0][2], s[t][0][3]));
+      mx = fmaxf(mx, fmaxf(fmaxf(s[t][1][0], s[t][1][1]), fmaxf(s[t][1][2], s[t][1][3])));
       // Move the reference (and rescale) only on a large increase; -inf -> finite always
       // moves. The test first uses this lane's own scores: only when some lane would move
       // is the row max formed across the row's four lanes (rare after the first step).
-      const bool grow_lane = mx * c > st.m[t] * c + RESCALE_LOG2 || (st.m[t] == NEG_INF && mx != NEG_INF);
-      if (__any(grow_lane)) {
+      if (__any(mx > st.thr[t])) {
         mx = max4(mx);
-        const bool grow = mx * c > st.m[t] * c + RESCALE_LOG2 || (st.m[t] == NEG_INF && mx != NEG_INF);
-        const float mnew = grow ? mx : st.m[t];
-        const float alpha = grow ? (st.m[t] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((st.m[t] - mnew) * c)) : 1.f;
-        st.m[t] = mnew;
-        st.l[t] *= alpha;
-        st.ls[t] *= alpha;
+        if (mx > st.thr[t]) {
+          const float alpha = st.m[t] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((st.m[t] - mx) * c);
+          st.m[t] = mx;
+          st.thr[t] = mx + RESCALE_LOG2 * inv_c;
+          st.nmc[t] = -mx * c;
+          st.l[t] *= alpha;
+          st.ls[t] *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) st.o[t][dt] *= alpha;
+          for (int dt = 0; dt < C::DT; ++dt) st.o[t][dt] *= alpha;
+        }
       }
-      const float mc = st.m[t] == NEG_INF ? 0.f : st.m[t] * c;
-      float psum = 0.f;
+      float pe[NT][4];
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][tt][e], c, -mc));
-          psum += pe;
-          p[t][tt][e] = (__bf16)pe;
+          pe[tt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][tt][e], c, st.nmc[t]));
+          p[t][tt][e] = (__bf16)pe[tt][e];
         }
-      st.l[t] += psum;
+      st.l[t] += ((pe[0][0] + pe[0][1]) + (pe[0][2] + pe[0][3])) + ((pe[1][0] + pe[1][1]) + (pe[1][2] + pe[1][3]));
     }
   }
 
-  const int e = li >> 2, cc = li & 3;
-  const int r0 = tok + 4 * G + e, r1 = r0 + 16;
   i16x4 lo[C::DT], hi[C::DT];
-  unsigned alo[C::DT], ahi[C::DT];
-#pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) {
-    const int ch = 2 * dt + (cc >> 1), off = 8 * (cc & 1);
-    alo[dt] = lds_addr(vt + r0 * C::ROWB + 16 * swz_v<D>(r0, ch) + off);
-    ahi[dt] = lds_addr(vt + r1 * C::ROWB + 16 * swz_v<D>(r1, ch) + off);
-  }
-  tr_read_all<C::DT>(lo, hi, alo, ahi);
+  tr_read<KOFF * C::ROWB, 16 * C::ROWB>(lo, hi, va);
   bf16x8 vop[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
@@ -369,68 +433,65 @@ __device__ __forceinline__ void softmax_step(State<D>& st, int nt, const unsigne
       st.ls[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, st.ls[t], 0, 0, 0);
     }
   }
-
 }
 
 // Normalise and store one row tile of a finished job (row li of the tile, dims
-// 16dt+4G..+3).
+// 16dt+4G..+3): Cfg<D>::STORES store instructions with every lane active. Lanes of
+// rows past the last query row store that row's values again.
 template <int D>
-__device__ __forceinline__ void write_tile(const State<D>& st, int t, const PartialArgs& a, const Job& J, int tile) {
+__device__ __forceinline__ void write_tile(const State<D>& st, int t, const PartialArgs& a, const Work& w, int tile) {
   using C = Cfg<D>;
   const int lane = threadIdx.x & 63;
   const int G = lane >> 4, li = lane & 15;
   const float l = sum4(st.l[t]);
-  const int row = tile * 16 + li;
-  if (row >= J.R) return;
+  const int row = tile_row(w.j, tile, li);
   const float ls = st.ls[t][0];
   const float inv = ls > 0.f ? 1.f / ls : 0.f;
   const float lse = l > 0.f ? st.m[t] * a.scale + __builtin_amdgcn_logf(l) * LN2 : NEG_INF;
   float* op;
   float* lp;
-  if (J.direct) {
+  if (a.out != nullptr && (w.j.flags & kJobSingle)) {
     const int i = row / a.g, hl = row - i * a.g;
-    const int64_t idx = (J.sq.q_base + i) * a.Hq + J.kv * a.g + hl;
+    const int64_t idx = (w.j.q_tok + i) * a.Hq + w.j.kv * a.g + hl;
     op = a.out + idx * D;
     lp = a.lse + idx;
   } else {
-    const int64_t prow = J.sq.row_base + (int64_t(J.kv) * J.sq.nb + J.block) * J.R + row;
+    const int64_t prow = w.j.ws_row + row;
     op = a.ws_o + prow * D;
     lp = a.ws_lse + prow;
   }
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) *reinterpret_cast<f32x4*>(op + 16 * dt + 4 * G) = st.o[t][dt] * inv;
-  if (G == 0) *lp = lse;
+  *lp = lse;
 }
 
-// Finish job J right after its last stage: combine its key slices (Wk > 1) through
+// Finish the job right after its last stage: combine its key slices (Wk > 1) through
 // the LDS slot that stage used, then store every row tile. The slot is next written by
-// DMA only after the following iteration's barrier. (Finishing before that iteration's
-// DMA issue instead delays the pipeline more than the stores cost here.)
+// DMA only after the following iteration's barrier. Returns the number of store
+// instructions this wave issued.
 template <int D>
-__device__ __forceinline__ void finish_job(State<D>& st, const PartialArgs& a, const Job& J, unsigned char* slot,
-                                           int wave, float c) {
+__device__ __forceinline__ int finish_job(State<D>& st, const PartialArgs& a, const Work& w, unsigned char* slot,
+                                          float c) {
   using C = Cfg<D>;
   const int lane = threadIdx.x & 63;
-  const int rg = wave % J.Wr, ks = wave / J.Wr;
-  const int ntw = ks < J.Wk && J.tile_hi - J.tile_lo - rg > 0 ? (J.tile_hi - J.tile_lo - rg + J.Wr - 1) / J.Wr : 0;
-  const int nt = min(ntw, RTW);
-  if (J.Wk == 1) {
+  const int Wr = 1 << w.wr_log;
+  if (w.Wk == 1) {
 #pragma unroll
     for (int t = 0; t < RTW; ++t)
-      if (t < nt) write_tile<D>(st, t, a, J, J.tile_lo + rg + t * J.Wr);
-    return;
+      if (t < w.nt) write_tile<D>(st, t, a, w, w.j.tile_lo + w.rg + t * Wr);
+    return w.nt * C::STORES;
   }
   // Two key slices per row group; one round per tile index (<= Wr records each). The
   // loop is unrolled with compile-time tile indices: a runtime index would put the
   // wave state in scratch memory.
   float* mbuf = reinterpret_cast<float*>(slot);
-  const int rounds = (J.tile_hi - J.tile_lo + J.Wr - 1) / J.Wr;
+  const int rounds = (w.j.tile_n + Wr - 1) >> w.wr_log;
 #pragma unroll
   for (int t = 0; t < RTW; ++t) {
     if (t >= rounds) break;
     lds_barrier();  // all waves are done with the slot's tiles / the previous round
-    if (ks == 1 && t < nt) {
-      float* rec = mbuf + rg * C::MSLOT;
+    if (w.ks == 1 && t < w.nt) {
+      float* rec = mbuf + w.rg * C::MSLOT;
       rec[lane] = st.m[t];
       rec[64 + lane] = st.l[t];
       rec[128 + lane] = st.ls[t][0];
@@ -440,8 +501,8 @@ __device__ __forceinline__ void finish_job(State<D>& st, const PartialArgs& a, c
         for (int q4 = 0; q4 < 4; ++q4) rec[(3 + dt * 4 + q4) * 64 + lane] = st.o[t][dt][q4];
     }
     lds_barrier();
-    if (ks == 0 && t < nt) {
-      const float* rec = mbuf + rg * C::MSLOT;
+    if (w.ks == 0 && t < w.nt) {
+      const float* rec = mbuf + w.rg * C::MSLOT;
       const float m2 = rec[lane];
       const float ms = fmaxf(st.m[t], m2);
       if (ms != NEG_INF) {
@@ -457,131 +518,148 @@ __device__ __forceinline__ void finish_job(State<D>& st, const PartialArgs& a, c
             st.o[t][dt][q4] = st.o[t][dt][q4] * a1 + rec[(3 + dt * 4 + q4) * 64 + lane] * a2;
         st.m[t] = ms;
       }
-      write_tile<D>(st, t, a, J, J.tile_lo + rg + t * J.Wr);
+      write_tile<D>(st, t, a, w, w.j.tile_lo + w.rg + t * Wr);
     }
   }
+  return w.ks == 0 ? w.nt * C::STORES : 0;
 }
 
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
-void partial_bf16_kernel(PartialArgs a, const UnitRec* __restrict__ units, const SeqRec* __restrict__ seqs,
-                         const int32_t* __restrict__ worker_ptr) {
+void partial_bf16_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const int32_t* __restrict__ job_ptr) {
   using C = Cfg<D>;
-  const Plan P{units, seqs};
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDSB];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int G = lane >> 4, li = lane & 15;
   const float c = a.scale * LOG2E;
+  const float inv_c = 1.f / c;
 
-  const int u_beg = worker_ptr[blockIdx.x], u_end = worker_ptr[blockIdx.x + 1];
-  if (u_beg >= u_end) return;
+  const int j_beg = job_ptr[blockIdx.x], j_end = job_ptr[blockIdx.x + 1];
+  if (j_beg >= j_end) return;
 
-  // Loader and compute walk the same job sequence; the loader runs two stages ahead.
-  Job L, J;
-  L.ui = J.ui = u_beg;
-  L.kv = J.kv = P.units[u_beg].kv0;
-  L.pass = J.pass = 0;
-  describe(a, P, L);
-  describe(a, P, J);
-  int lj = 0;         // next stage of job L to issue
-  bool lmore = true;  // loader has stages left
-  int last_cnt = 0;   // vector-memory instructions of the most recently issued stage
-  int issued = 0;     // stages issued so far
+  const uint32_t kst = uint32_t(a.k_st) * 2, vst = uint32_t(a.v_st) * 2;  // bytes per token
+  LaneOff<D> lo;
+  lane_offsets<D>(lo, wave, lane, kst, vst);
+
+  // Vector-memory instructions this wave issued after the most recent stage's DMA (c1)
+  // and after the stage before it (c2).
+  int c1 = 0, c2 = 0;
+  Loader L;
+  L.job = j_beg;
+  L.end = j_end;
+  open_job(L, a, jobs);
+  bool lmore = true;
+  int issued = 0;
+  int slot_l = 0;  // slot of the next stage to issue
   for (int k = 0; k < NST - 1 && lmore; ++k) {
-    last_cnt = issue_stage<D>(a, L, lj, smem + (issued % NST) * C::SLOTB, wave, lane);
+    const int n = issue_stage<D>(a, jobs, L, smem + slot_l * C::SLOTB, lo, wave, lane, kst, vst);
+    c2 = c1 + n;
+    c1 = 0;
     ++issued;
-    if (++lj == L.nst) {
-      lj = 0;
-      lmore = next_job(P, L, u_end);
-      if (lmore) describe(a, P, L);
+    ++slot_l;
+    if (L.stage == L.nst) {
+      lmore = ++L.job < L.end;
+      if (lmore) open_job(L, a, jobs);
     }
   }
 
+  Work w;
+  w.job = j_beg;
+  open_work(w, jobs, wave, a.g);
   State<D> st;
-  int jj = 0;  // stage within the compute job
+  int slot_c = 0;  // slot of the stage computed
   for (int i = 0;; ++i) {
-    // Stage i landed (for every wave) once the later stages are all that is pending.
-    // Here at most stage i + 1 was issued after it, and it is the latest one.
-    wait_vm_barrier(issued > i + 1 ? last_cnt : 0);
+    // Stage i landed (for every wave) once the later stages' DMA and the stores after
+    // them are all that is pending; stage i + 1, if issued, is the most recent stage.
+    wait_stage<D>(issued > i + 1 ? c2 : c1);
+    unsigned char* slot = smem + slot_c * C::SLOTB;
 
-    // This wave's share of the job.
-    const int rg = wave % J.Wr, ks = wave / J.Wr;
-    const int ntw = ks < J.Wk && J.tile_hi - J.tile_lo - rg > 0 ? (J.tile_hi - J.tile_lo - rg + J.Wr - 1) / J.Wr : 0;
-    const int nt = min(ntw, RTW);
-    if (jj == 0 && !J.qlds) {
-      // Job start with Q from HBM: issued before this iteration's DMA, so that waiting
-      // for it leaves the newer stages in flight.
+    if (w.jj == 0) {
+      // Job start: per-row limits, Q operands, accumulators.
+      const int Wr = 1 << w.wr_log;
 #pragma unroll
       for (int t = 0; t < RTW; ++t) {
-        const int row = (J.tile_lo + rg + t * J.Wr) * 16 + li;
-        const bool ok = t < nt && row < J.R;
-        const int iq = ok ? row / a.g : 0;
-        const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + (J.sq.q_base + iq) * a.q_st +
-                           int64_t(J.kv * a.g + (ok ? row - iq * a.g : 0)) * a.q_sh + 8 * G;
-#pragma unroll
-        for (int dc = 0; dc < C::DC; ++dc)
-          st.q[t][dc] = ok ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * dc)) : bf16x8{};
+        const int row = tile_row(w.j, w.j.tile_lo + w.rg + t * Wr, li);
+        st.lim[t] = min(w.j.lim0 + row / a.g, w.j.len - 1);
       }
-      // Complete these loads here (only the previous stage's DMA is older). A compiler-
-      // visible wait, so that no load into the Q registers is pending anywhere else in
-      // the loop: otherwise every later use of them would wait for all in-flight DMA.
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    }
-    if (lmore) {
-      last_cnt = issue_stage<D>(a, L, lj, smem + (issued % NST) * C::SLOTB, wave, lane);
-      ++issued;
-      if (++lj == L.nst) {
-        lj = 0;
-        lmore = next_job(P, L, u_end);
-        if (lmore) describe(a, P, L);
-      }
-    }
-    unsigned char* slot = smem + (i % NST) * C::SLOTB;
-    if (jj == 0) {
-      // Job start: Q operands, accumulators, per-row limits.
+      if (!(w.j.flags & kJobQTile)) {
+        // Q from HBM, loaded before this iteration's DMA is issued.
 #pragma unroll
-      for (int t = 0; t < RTW; ++t) {
-        const int tile = J.tile_lo + rg + t * J.Wr;
-        const int row = tile * 16 + li;
-        const bool ok = t < nt && row < J.R;
-        const int iq = ok ? row / a.g : 0;
-        st.lim[t] = a.causal ? min(J.lim0 + iq, J.len - 1) : J.len - 1;
-        if (J.qlds) {
-          // The Q tile of this slot holds rows 0..63 of the unit (R <= 64 here).
-          const int qr = t < nt ? row : 0;
+        for (int t = 0; t < RTW; ++t) {
+          const int row = tile_row(w.j, w.j.tile_lo + w.rg + t * Wr, li);
+          const int iq = row / a.g;
+          const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + (w.j.q_tok + iq) * a.q_st +
+                             int64_t(w.j.kv * a.g + (row - iq * a.g)) * a.q_sh + 8 * G;
 #pragma unroll
           for (int dc = 0; dc < C::DC; ++dc)
-            st.q[t][dc] = *reinterpret_cast<const bf16x8*>(slot + 2 * C::TILEB + qr * C::ROWB +
-                                                           16 * swz_k<D>(qr, 4 * dc + G));
+            st.q[t][dc] = t < w.nt ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * dc))
+                                   : bf16x8{};
         }
+        // Complete these loads here. A compiler-visible wait, so that no load into the Q
+        // registers is pending anywhere else in the loop: otherwise every later use of
+        // them would wait for all in-flight DMA. Nothing this wave issued is pending
+        // after it.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        c1 = 0;
+        c2 = 0;
+      } else {
+        // The Q tile of this slot holds rows 0..63 of the job.
+#pragma unroll
+        for (int t = 0; t < RTW; ++t) {
+          const int tile = w.j.tile_lo + w.rg + t * Wr;
+          const unsigned qa = lds_addr(slot + 2 * C::TILEB) + unsigned(t < w.nt ? tile : 0) * (16 * C::ROWB);
+#pragma unroll
+          for (int dc = 0; dc < C::DC; ++dc) st.q[t][dc] = *reinterpret_cast<lds_bf16x8>(uintptr_t(qa + lo.kr[dc]));
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < RTW; ++t) {
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) st.o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         st.m[t] = NEG_INF;
+        st.thr[t] = NEG_INF;
+        st.nmc[t] = 0.f;
         st.l[t] = 0.f;
         st.ls[t] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
 
-    // Keys of this stage handled by this wave, and whether masking is needed.
-    const int tkw = TK / J.Wk;
-    const int tok_w = ks * tkw;
-    const int tok_stage = jj * TK;
-    const int first_row = (J.tile_lo + rg) * 16;
-    const int min_lim = a.causal ? J.lim0 + min(first_row, J.R - 1) / a.g : J.len - 1;
-    const int last_key = tok_stage + tok_w + tkw - 1;
-    const bool need_mask = last_key >= J.len || last_key > min_lim;
-    if (nt > 0) {
-      for (int h = 0; h < tkw; h += 32) softmax_step<D>(st, nt, slot, tok_stage, tok_w + h, need_mask, c);
+    if (lmore) {
+      const int n = issue_stage<D>(a, jobs, L, smem + slot_l * C::SLOTB, lo, wave, lane, kst, vst);
+      c2 = c1 + n;
+      c1 = 0;
+      ++issued;
+      slot_l = slot_l == NST - 1 ? 0 : slot_l + 1;
+      if (L.stage == L.nst) {
+        lmore = ++L.job < L.end;
+        if (lmore) open_job(L, a, jobs);
+      }
     }
-    if (jj + 1 == J.nst) {
-      finish_job<D>(st, a, J, slot, wave, c);
-      jj = 0;
-      if (!next_job(P, J, u_end)) break;
-      describe(a, P, J);
+
+    // This wave's keys of the stage: block keys [key0, key0 + tkw).
+    const int key0 = w.jj * TK + w.tok_w;
+    if (w.nt > 0 && key0 <= w.max_lim) {
+      const bool need_mask = key0 + w.tkw - 1 > w.min_lim;
+      const unsigned sb = lds_addr(slot) + unsigned(w.tok_w) * C::ROWB;
+      unsigned ka[C::DC], va[C::DT];
+#pragma unroll
+      for (int dc = 0; dc < C::DC; ++dc) ka[dc] = sb + lo.kr[dc];
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) va[dt] = sb + C::TILEB + lo.vr[dt];
+      softmax_step<D, 0>(st, w.nt, ka, va, key0, need_mask, c, inv_c);
+      if (w.tkw == TK) softmax_step<D, 32>(st, w.nt, ka, va, key0 + 32, need_mask, c, inv_c);
+    }
+    if (w.jj + 1 == w.j.nst) {
+      const int s = finish_job<D>(st, a, w, slot, c);
+      c1 += s;
+      c2 += s;
+      if (++w.job >= j_end) break;
+      open_work(w, jobs, wave, a.g);
     } else {
-      ++jj;
+      ++w.jj;
     }
+    slot_c = slot_c == NST - 1 ? 0 : slot_c + 1;
   }
 }
 
@@ -590,9 +668,9 @@ void partial_bf16_kernel(PartialArgs a, const UnitRec* __restrict__ units, const
 hipError_t launch_partial_bf16(const PartialArgs& a, int head_dim, hipStream_t stream) {
   dim3 grid(a.num_workers), block(NW * 64);
   if (head_dim == 128)
-    hipLaunchKernelGGL(partial_bf16_kernel<128>, grid, block, 0, stream, a, a.units, a.seqs, a.worker_ptr);
+    hipLaunchKernelGGL(partial_bf16_kernel<128>, grid, block, 0, stream, a, a.jobs, a.job_ptr);
   else if (head_dim == 64)
-    hipLaunchKernelGGL(partial_bf16_kernel<64>, grid, block, 0, stream, a, a.units, a.seqs, a.worker_ptr);
+    hipLaunchKernelGGL(partial_bf16_kernel<64>, grid, block, 0, stream, a, a.jobs, a.job_ptr);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

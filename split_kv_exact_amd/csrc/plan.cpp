@@ -192,6 +192,50 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   off = align16(off + sizeof(int32_t) * uint64_t(std::max(pl->num_multi, 1)));
   L.merge_multi_base = off;
   off = align16(off + sizeof(int64_t) * uint64_t(pl->num_multi + 1));
+
+  // Jobs of the bf16 kernel, worker by worker in unit order: for each unit its KV
+  // heads, for each head its row passes.
+  std::vector<JobRec> jobs;
+  std::vector<int32_t> job_ptr(m + 1, 0);
+  for (int32_t w = 0; w < m; ++w) {
+    for (int32_t i = pl->worker_ptr[w]; i < pl->worker_ptr[w + 1]; ++i) {
+      const int32_t u = pl->worker_units[i];
+      const SeqRec& r = pl->seqs[pl->u_seq[u]];
+      const int32_t b = pl->u_block[u];
+      const int64_t key0 = int64_t(b) * B;
+      const int32_t len = pl->u_len[u];
+      // Query token i sees keys up to n - q + i, i.e. block keys t <= (n - q - key0) + i.
+      const int32_t lim0 = pl->causal ? int32_t(std::min<int64_t>(len, r.n - r.q - key0)) : len;
+      const int32_t nrt = (r.rows + 15) / 16;
+      const int32_t kv_lo = per_head ? pl->u_kv[u] : 0, kv_hi = per_head ? kv_lo + 1 : Hkv;
+      for (int32_t kv = kv_lo; kv < kv_hi; ++kv) {
+        for (int32_t t0 = 0; t0 < nrt; t0 += kPassTiles) {
+          JobRec j{};
+          j.kv_tok = r.kv_base + key0;
+          j.q_tok = r.q_base;
+          j.ws_row = r.row_base + (int64_t(kv) * r.nb + b) * r.rows;
+          j.kv = kv;
+          j.len = len;
+          j.lim0 = lim0;
+          j.rows = r.rows;
+          j.tile_lo = t0;
+          j.tile_n = std::min(kPassTiles, nrt - t0);
+          const int32_t rmax = std::min(r.rows, (t0 + j.tile_n) * 16) - 1;
+          const int64_t tmax = std::min<int64_t>(len - 1, int64_t(lim0) + rmax / g);
+          j.nst = tmax < 0 ? 1 : int32_t(tmax / kStageKeys) + 1;
+          const int32_t wr_log = j.tile_n >= 8 ? 3 : j.tile_n >= 4 ? 2 : j.tile_n >= 2 ? 1 : 0;
+          j.flags = wr_log | (r.rows <= kQTileRows ? kJobQTile : 0) | (r.nb == 1 ? kJobSingle : 0);
+          jobs.push_back(j);
+        }
+      }
+    }
+    job_ptr[w + 1] = int32_t(jobs.size());
+  }
+  pl->num_jobs = int64_t(jobs.size());
+  L.jobs = off;
+  off = align16(off + sizeof(JobRec) * jobs.size());
+  L.job_ptr = off;
+  off = align16(off + sizeof(int32_t) * uint64_t(m + 1));
   L.total = off;
 
   pl->image.assign(L.total, 0);
@@ -221,6 +265,8 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
       ++j;
     }
   }
+  if (!jobs.empty()) std::memcpy(base + L.jobs, jobs.data(), sizeof(JobRec) * jobs.size());
+  std::memcpy(base + L.job_ptr, job_ptr.data(), sizeof(int32_t) * (m + 1));
 }
 
 }  // namespace splitkv

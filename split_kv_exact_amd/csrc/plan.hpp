@@ -31,6 +31,7 @@ struct splitkv_plan_s {
   int64_t merge_rows_all = 0, merge_rows_multi = 0;
   int32_t num_multi = 0;  // sequences with more than one block
   int32_t max_rows = 0;   // max_s q_s * g
+  int64_t num_jobs = 0;   // jobs of the bf16 kernel
   size_t ws_bytes = 0, ws_lse_offset = 0;
 
   // Device image.

@@ -30,6 +30,38 @@ struct UnitRec {
 };
 static_assert(sizeof(UnitRec) == 16, "UnitRec layout");
 
+// Keys per stage of the bf16 partial-attention pipeline, and the largest row count
+// whose Q tile travels with a job's first stage. The planner uses both to cut units
+// into jobs.
+constexpr int32_t kStageKeys = 64;
+constexpr int32_t kQTileRows = 64;
+// Row tiles of 16 query rows that one pass of the bf16 kernel covers.
+constexpr int32_t kPassTiles = 16;
+
+// Job flags.
+constexpr int32_t kJobWrMask = 3;   // log2 of the row groups the 8 wavefronts form
+constexpr int32_t kJobQTile = 4;    // Q rows of the job travel through LDS with stage 0
+constexpr int32_t kJobSingle = 8;   // the sequence has a single block (its result is final)
+
+// One job of the bf16 partial-attention kernel: one pass over a block's keys for one
+// KV head and up to kPassTiles row tiles of its query rows. Query row r of a KV head
+// is query token i = r / g of the sequence, query head kv * g + r % g.
+struct JobRec {
+  int64_t kv_tok;   // token of the block's first key in K / V
+  int64_t q_tok;    // token of the sequence's first query in Q / out / lse
+  int64_t ws_row;   // workspace row of query row 0 for this (KV head, block)
+  int32_t kv;       // KV head
+  int32_t len;      // keys in the block
+  int32_t lim0;     // causal: query token i sees block keys t <= lim0 + i
+  int32_t rows;     // query rows of the KV head, q_s * g
+  int32_t tile_lo;  // first row tile of this pass
+  int32_t tile_n;   // row tiles in this pass
+  int32_t nst;      // stages of kStageKeys keys that hold a visible key
+  int32_t flags;    // kJob* bits
+  int32_t pad[2];
+};
+static_assert(sizeof(JobRec) == 64, "JobRec layout");
+
 // Offsets of the arrays inside the image.
 struct ImageLayout {
   uint64_t seqs;        // SeqRec[S]
@@ -38,6 +70,8 @@ struct ImageLayout {
   uint64_t merge_all;   // int64[S + 1]: prefix of Hkv * rows over all sequences
   uint64_t merge_multi; // int32[S_multi] sequence ids with nb > 1, then
   uint64_t merge_multi_base;  // int64[S_multi + 1]: prefix of Hkv * rows over them
+  uint64_t jobs;        // JobRec[num_jobs], grouped by worker (worker order)
+  uint64_t job_ptr;     // int32[m + 1]: worker w owns jobs [job_ptr[w], job_ptr[w+1])
   uint64_t total;
 };
 
