@@ -136,6 +136,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="skip the cold-cache per-step measurement")
+    ap.add_argument("--schedule", default="auto", choices=("auto", "queue", "static"),
+                    help="how the partial-attention workgroups take their jobs (bf16)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (a kernel of known traffic, for scaling "
                          "hardware byte counters)")
@@ -175,11 +177,13 @@ def main() -> int:
     lse = torch.empty((wl.total_q, wl.num_q_heads), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
+    sched = args.schedule
+
     def step():
-        skv.splitkv_attn(plan, dev_plan, q, k, v, ws, out, lse)
+        skv.splitkv_attn(plan, dev_plan, q, k, v, ws, out, lse, schedule=sched)
 
     def partial():
-        skv.splitkv_partial_attn(plan, dev_plan, q, k, v, ws)
+        skv.splitkv_partial_attn(plan, dev_plan, q, k, v, ws, schedule=sched)
 
     def merge():
         skv.splitkv_merge(plan, dev_plan, ws, out, lse)
@@ -207,6 +211,29 @@ def main() -> int:
     # Dominant kernel (partial attention) and merge, each launched alone, back to back.
     ms_partial = _time_loop(partial, args.steps, stream)
     ms_merge = _time_loop(merge, args.steps, stream)
+    # Per-step spread: each fused step timed alone (median and minimum).
+    per_step = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        per_step.append(e0.elapsed_time(e1))
+    per_step.sort()
+    # Measured per-CU time imbalance of one partial-attention launch: each workgroup's
+    # start and end on the GPU's 100 MHz clock.
+    clock = torch.zeros(2 * wl.num_workers, dtype=torch.int64, device=dev)
+    skv.splitkv_partial_attn(plan, dev_plan, q, k, v, ws, schedule=sched, clock=clock)
+    torch.cuda.synchronize()
+    ck = clock.view(-1, 2).cpu().double()
+    busy = (ck[:, 1] - ck[:, 0]) / 100.0  # microseconds
+    measured = {
+        "busy_us_mean": round(float(busy.mean()), 2),
+        "busy_us_max": round(float(busy.max()), 2),
+        "imbalance": round(float(busy.max() / busy.mean() - 1.0), 4),
+        "end_spread_us": round(float((ck[:, 1].max() - ck[:, 1].min()) / 100.0), 2),
+    }
     ms_cold = None
     if not args.no_flush:
         flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -254,6 +281,8 @@ def main() -> int:
             "ms_per_launch": round(ms_partial, 5),
             "algorithmic_bytes_per_launch": pk_bytes,
         },
+        "ms_per_step_median": round(per_step[len(per_step) // 2], 5),
+        "ms_per_step_min": round(per_step[0], 5),
         "ms_merge_kernel": round(ms_merge, 5),
         "ms_per_step_cold_cache": None if ms_cold is None else round(ms_cold, 5),
         "wall_ms_per_step": round(wall_ms, 5),
@@ -266,6 +295,8 @@ def main() -> int:
             "makespan": info["makespan"],
             "lower_bound": info["lower_bound"],
             "plan_ms_median": round(plan_times[len(plan_times) // 2], 4),
+            "schedule": sched,
+            "measured_per_cu": measured,
         },
         "workspace_bytes": info["workspace_bytes"],
         "kernel_sha": _kernel_sha(),

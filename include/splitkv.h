@@ -52,7 +52,7 @@ extern "C" {
 #endif
 
 #define SPLITKV_VERSION_MAJOR 0
-#define SPLITKV_VERSION_MINOR 1
+#define SPLITKV_VERSION_MINOR 2
 
 typedef enum {
   SPLITKV_OK = 0,
@@ -69,6 +69,26 @@ typedef enum { SPLITKV_F32 = 0, SPLITKV_BF16 = 1 } splitkv_dtype;
  * one KV head is the default unit (it serves g = Hq/Hkv query heads), a whole block
  * serving all Hq query heads is the coarser alternative. */
 typedef enum { SPLITKV_UNIT_SEQ_BLOCK_KVHEAD = 0, SPLITKV_UNIT_SEQ_BLOCK = 1 } splitkv_granularity;
+
+/* How the workgroups of a bf16 partial-attention launch take their jobs (a job is one
+ * unit's KV head and up to 256 of its query rows; jobs are numbered in LPT order:
+ * unit cost descending, ties in enumeration order).
+ *   SPLITKV_SCHED_STATIC workgroup w runs the units the plan gave worker w, in order.
+ *   SPLITKV_SCHED_QUEUE  workgroup w runs the plan's worker w units except the
+ *                        cheapest ones at the end of the LPT order (about a fifth
+ *                        of the estimated time, estimate = keys * max(rows, 128));
+ *                        those form a shared tail, cut into chunks and dealt over 8
+ *                        sub-queues, from which every workgroup draws (its own
+ *                        sub-queue first) whenever it frees up: LPT's rule "next job
+ *                        to the first free worker" applied at run time, so workgroups
+ *                        that run faster (the CUs differ in memory bandwidth) take
+ *                        more of the tail.
+ *   SPLITKV_SCHED_AUTO   QUEUE when the plan has at least 24 jobs per workgroup
+ *                        (otherwise one chunk is too large a share to balance by),
+ *                        else STATIC.
+ * All give bitwise identical results (a job's output does not depend on where it
+ * runs). fp32 launches always use the static assignment. */
+typedef enum { SPLITKV_SCHED_AUTO = 0, SPLITKV_SCHED_QUEUE = 1, SPLITKV_SCHED_STATIC = 2 } splitkv_schedule;
 
 /* Problem description. Host memory, caller-owned, read only during splitkv_plan. */
 typedef struct {
@@ -111,6 +131,12 @@ typedef struct {
   int64_t v_stride_tok, v_stride_head;
   int32_t dtype;  /* splitkv_dtype, the same for q, k and v                          */
   float scale;    /* softmax scale; 0 selects 1/sqrt(head_dim)                       */
+  int32_t schedule;           /* splitkv_schedule (bf16 launches)                    */
+  uint64_t *worker_clock;     /* NULL, or device [2 * num_workers]: each workgroup of
+                                 the partial-attention launch writes the GPU's
+                                 constant 100 MHz clock when it starts and when it
+                                 has finished its jobs (entries 2w and 2w + 1); the
+                                 measured per-CU time imbalance comes from these.   */
 } splitkv_inputs;
 
 /* Version as (major << 16) | minor. */
@@ -140,7 +166,11 @@ int splitkv_plan_export(const splitkv_plan_t *plan, int32_t *unit_seq, int32_t *
 
 /* Copy the plan's device image (plan_bytes) to caller-owned device memory dev_plan
  * with an asynchronous host-to-device copy on hip_stream (NULL = default stream).
- * The plan must stay alive until that copy has completed.
+ * The plan must stay alive until that copy has completed. The image ends with a
+ * 1024-byte scheduling area (the counters of the SPLITKV_SCHED_QUEUE tail): the
+ * upload zeroes it, and every queue-scheduled launch updates it and leaves it zero
+ * again, so launches that use one plan buffer must not overlap in time (use one
+ * stream per plan buffer).
  * Errors: INVALID_ARG, WORKSPACE (bytes < plan_bytes), HIP. */
 int splitkv_plan_upload(const splitkv_plan_t *plan, void *dev_plan, size_t bytes, void *hip_stream);
 
@@ -149,13 +179,14 @@ void splitkv_plan_destroy(splitkv_plan_t *plan);
 
 /* Partial attention of every unit: for each context KV block and KV head, the output
  * and log-sum-exp of the queries against that block alone (the query-sized per-block
- * result of the Split-KV page's lede). One workgroup per LPT worker walks its unit
- * list. Writes the whole workspace (layout above); every row is written, rows that
- * see no key of a block get O = 0 and LSE = -inf.
+ * result of the Split-KV page's lede). One workgroup per LPT worker; in->schedule
+ * says how the workgroups take the jobs. Writes the whole workspace (layout above);
+ * every row is written, rows that see no key of a block get O = 0 and LSE = -inf.
+ * dev_plan is the uploaded plan; the launch also uses its scheduling area.
  * Errors: INVALID_ARG (null/misaligned pointers, strides), UNSUPPORTED (no kernel for
  * dtype/head_dim, bf16 stride above 2^24), WORKSPACE (ws_bytes < workspace_bytes),
  * HIP (launch failed). */
-int splitkv_partial_attn(const splitkv_plan_t *plan, const void *dev_plan, const splitkv_inputs *in,
+int splitkv_partial_attn(const splitkv_plan_t *plan, void *dev_plan, const splitkv_inputs *in,
                          float *ws, size_t ws_bytes, void *hip_stream);
 
 /* Log-sum-exp merge of the partials in the workspace into out [sum q, Hq, D] and
@@ -169,7 +200,7 @@ int splitkv_merge(const splitkv_plan_t *plan, const void *dev_plan, const float 
 /* Fused call: partial attention and merge enqueued back to back on hip_stream, with
  * sequences of a single block written straight to out/lse. Same arguments and errors
  * as the two calls above. */
-int splitkv_attn(const splitkv_plan_t *plan, const void *dev_plan, const splitkv_inputs *in,
+int splitkv_attn(const splitkv_plan_t *plan, void *dev_plan, const splitkv_inputs *in,
                  float *ws, size_t ws_bytes, float *out, float *lse, void *hip_stream);
 
 /* Static text for a status code. */

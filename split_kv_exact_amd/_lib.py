@@ -25,6 +25,10 @@ SPLITKV_BF16 = 1
 SPLITKV_UNIT_SEQ_BLOCK_KVHEAD = 0
 SPLITKV_UNIT_SEQ_BLOCK = 1
 
+SPLITKV_SCHED_AUTO = 0
+SPLITKV_SCHED_QUEUE = 1
+SPLITKV_SCHED_STATIC = 2
+
 # Every function include/splitkv.h declares.
 EXPORTED = (
     "splitkv_version",
@@ -85,6 +89,8 @@ class Inputs(ctypes.Structure):
         ("v_stride_head", ctypes.c_int64),
         ("dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
+        ("schedule", ctypes.c_int32),
+        ("worker_clock", ctypes.c_void_p),
     ]
 
 

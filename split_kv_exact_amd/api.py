@@ -154,7 +154,10 @@ def workspace_views(plan: Plan, ws) -> Tuple[object, object]:
     return ws[: rows * d].view(rows, d), ws[off: off + rows]
 
 
-def _inputs(q, k, v, scale: float) -> L.Inputs:
+_SCHEDULES = {"auto": L.SPLITKV_SCHED_AUTO, "queue": L.SPLITKV_SCHED_QUEUE, "static": L.SPLITKV_SCHED_STATIC}
+
+
+def _inputs(q, k, v, scale: float, schedule: str = "auto", clock=None) -> L.Inputs:
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dim() != 3 or t.stride(2) != 1:
@@ -173,6 +176,8 @@ def _inputs(q, k, v, scale: float) -> L.Inputs:
         k_stride_tok=k.stride(0), k_stride_head=k.stride(1),
         v_stride_tok=v.stride(0), v_stride_head=v.stride(1),
         dtype=dt, scale=float(scale),
+        schedule=_SCHEDULES[schedule] if schedule in _SCHEDULES else int(schedule),
+        worker_clock=None if clock is None else clock.data_ptr(),
     )
 
 
@@ -186,12 +191,18 @@ def _check_shapes(plan: Plan, q, k, v) -> None:
             raise ValueError(f"{name} has shape {tuple(t.shape)}, plan expects {(tk, p['num_kv_heads'], p['head_dim'])}")
 
 
-def splitkv_partial_attn(plan: Plan, dev_plan, q, k, v, ws=None, scale: float = 0.0, stream=None):
-    """Per-block partial outputs and LSEs into the workspace (``splitkv_partial_attn``)."""
+def splitkv_partial_attn(plan: Plan, dev_plan, q, k, v, ws=None, scale: float = 0.0, stream=None,
+                         schedule: str = "auto", clock=None):
+    """Per-block partial outputs and LSEs into the workspace (``splitkv_partial_attn``).
+
+    ``schedule`` is "auto", "queue" (the cheapest jobs form a tail shared at run
+    time) or "static" (each workgroup runs its plan worker's units); ``clock`` is
+    None or an int64 device tensor of
+    2 * num_workers entries that receives each workgroup's start and end clock."""
     _check_shapes(plan, q, k, v)
     if ws is None:
         ws = workspace(plan, q.device)
-    inp = _inputs(q, k, v, scale)
+    inp = _inputs(q, k, v, scale, schedule, clock)
     _check(plan._lib, plan._lib.splitkv_partial_attn(plan.handle, ctypes.c_void_p(dev_plan.data_ptr()),
                                                      ctypes.byref(inp), ctypes.c_void_p(ws.data_ptr()),
                                                      ws.numel() * ws.element_size(), _stream(stream)),
@@ -225,13 +236,15 @@ def splitkv_merge(plan: Plan, dev_plan, ws, out=None, lse=None, stream=None):
     return out, lse
 
 
-def splitkv_attn(plan: Plan, dev_plan, q, k, v, ws=None, out=None, lse=None, scale: float = 0.0, stream=None):
-    """Fused partial attention + merge (``splitkv_attn``)."""
+def splitkv_attn(plan: Plan, dev_plan, q, k, v, ws=None, out=None, lse=None, scale: float = 0.0, stream=None,
+                 schedule: str = "auto", clock=None):
+    """Fused partial attention + merge (``splitkv_attn``); ``schedule`` and ``clock`` as
+    for :func:`splitkv_partial_attn`."""
     _check_shapes(plan, q, k, v)
     if ws is None:
         ws = workspace(plan, q.device)
     out, lse = _outputs(plan, q.device, out, lse)
-    inp = _inputs(q, k, v, scale)
+    inp = _inputs(q, k, v, scale, schedule, clock)
     _check(plan._lib, plan._lib.splitkv_attn(plan.handle, ctypes.c_void_p(dev_plan.data_ptr()), ctypes.byref(inp),
                                              ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
                                              ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse.data_ptr()),

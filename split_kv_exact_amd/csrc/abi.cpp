@@ -46,6 +46,11 @@ int check_inputs(const splitkv_plan_t* pl, const splitkv_inputs* in, float* scal
   for (int64_t x : st)
     if (x < 0 || x % vec != 0)
       return fail(SPLITKV_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
+  if (in->schedule != SPLITKV_SCHED_AUTO && in->schedule != SPLITKV_SCHED_QUEUE &&
+      in->schedule != SPLITKV_SCHED_STATIC)
+    return fail(SPLITKV_ERR_INVALID_ARG, "unknown schedule");
+  if ((reinterpret_cast<uintptr_t>(in->worker_clock) & 7u) != 0)
+    return fail(SPLITKV_ERR_INVALID_ARG, "worker_clock must be 8-byte aligned");
   // The bf16 kernel addresses a lane's rows within one stage or Q tile with 32-bit
   // byte offsets.
   if (in->dtype == SPLITKV_BF16)
@@ -74,7 +79,7 @@ int check_out(const float* out, const float* lse) {
   return SPLITKV_OK;
 }
 
-splitkv::PartialArgs partial_args(const splitkv_plan_t* pl, const void* dev_plan, const splitkv_inputs* in,
+splitkv::PartialArgs partial_args(const splitkv_plan_t* pl, void* dev_plan, const splitkv_inputs* in,
                                   float scale, float* ws) {
   const uint8_t* base = static_cast<const uint8_t*>(dev_plan);
   splitkv::PartialArgs a{};
@@ -92,7 +97,16 @@ splitkv::PartialArgs partial_args(const splitkv_plan_t* pl, const void* dev_plan
   a.units = reinterpret_cast<const splitkv::UnitRec*>(base + pl->layout.units);
   a.worker_ptr = reinterpret_cast<const int32_t*>(base + pl->layout.worker_ptr);
   a.jobs = reinterpret_cast<const splitkv::JobRec*>(base + pl->layout.jobs);
+  a.wjobs = reinterpret_cast<const int32_t*>(base + pl->layout.wjobs);
   a.job_ptr = reinterpret_cast<const int32_t*>(base + pl->layout.job_ptr);
+  a.sched = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(dev_plan) + pl->layout.sched);
+  a.chunk_ptr = reinterpret_cast<const int32_t*>(base + pl->layout.chunk_ptr);
+  a.num_jobs = int32_t(pl->num_jobs);
+  const bool queue = in->schedule == SPLITKV_SCHED_QUEUE || (in->schedule == SPLITKV_SCHED_AUTO && pl->queue_default);
+  a.queue = queue && pl->tail_start < pl->num_jobs ? 1 : 0;
+  a.tail_start = a.queue ? pl->tail_start : a.num_jobs;
+  a.num_chunks = int32_t(pl->chunk_ptr.size()) - 1;
+  a.clock = in->worker_clock;
   a.num_workers = pl->m;
   a.Hq = pl->Hq;
   a.Hkv = pl->Hkv;
@@ -214,7 +228,7 @@ int splitkv_plan_upload(const splitkv_plan_t* pl, void* dev_plan, size_t bytes, 
 
 void splitkv_plan_destroy(splitkv_plan_t* pl) { delete pl; }
 
-int splitkv_partial_attn(const splitkv_plan_t* pl, const void* dev_plan, const splitkv_inputs* in, float* ws,
+int splitkv_partial_attn(const splitkv_plan_t* pl, void* dev_plan, const splitkv_inputs* in, float* ws,
                          size_t ws_bytes, void* hip_stream) {
   g_last_error.clear();
   if (int st = check_plan(pl, dev_plan)) return st;
@@ -237,7 +251,7 @@ int splitkv_merge(const splitkv_plan_t* pl, const void* dev_plan, const float* w
   return hip_status(splitkv::launch_merge(m, pl->D, static_cast<hipStream_t>(hip_stream)), "merge launch");
 }
 
-int splitkv_attn(const splitkv_plan_t* pl, const void* dev_plan, const splitkv_inputs* in, float* ws, size_t ws_bytes,
+int splitkv_attn(const splitkv_plan_t* pl, void* dev_plan, const splitkv_inputs* in, float* ws, size_t ws_bytes,
                  float* out, float* lse, void* hip_stream) {
   g_last_error.clear();
   if (int st = check_plan(pl, dev_plan)) return st;

@@ -17,8 +17,16 @@ struct PartialArgs {
   const SeqRec* seqs;
   const UnitRec* units;
   const int32_t* worker_ptr;
-  const JobRec* jobs;       // bf16 kernel: jobs grouped by worker
-  const int32_t* job_ptr;   // bf16 kernel: worker w owns jobs [job_ptr[w], job_ptr[w+1])
+  const JobRec* jobs;       // bf16 kernel: jobs in LPT order
+  const int32_t* wjobs;     // bf16 kernel: job indices of each worker's units
+  const int32_t* job_ptr;   // bf16 kernel: worker w's jobs are wjobs[job_ptr[w] .. job_ptr[w+1])
+  uint32_t* sched;          // bf16 kernel: queue counters (next chunk, workgroups done), zero between launches
+  const int32_t* chunk_ptr; // bf16 kernel: the shared tail's chunks
+  int32_t num_jobs;
+  int32_t tail_start;       // bf16 kernel: jobs from here on come from the shared tail (num_jobs: none)
+  int32_t num_chunks;
+  int32_t queue;            // bf16 kernel: 1 = shared tail in use
+  uint64_t* clock;          // null, or [2 * num_workers] start / end clocks per workgroup
   int32_t num_workers;
   int32_t Hq, Hkv, g, B, causal;
   float* ws_o;    // partial outputs [partial_rows, D]

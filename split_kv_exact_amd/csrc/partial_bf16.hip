@@ -124,10 +124,8 @@ __device__ __forceinline__ void wait_stage(int n) {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(NKV) : "memory");
   else if (n == NKV + NQ)
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(NKV + NQ) : "memory");
-  else {
-    asm volatile("" : "+s"(n));  // keeps the tests above out of the switch below
-    wait_vm_barrier(n);
-  }
+  else
+    wait_vm_barrier(__builtin_amdgcn_readfirstlane(n));  // opaque: keeps the tests above out of the switch
 }
 
 // LDS writes and reads of this wave done, then barrier.
@@ -213,7 +211,7 @@ __device__ __forceinline__ void lane_offsets(LaneOff<D>& lo, int wave, int lane,
 
 // The DMA side of the pipeline: the job and stage to issue next.
 struct Loader {
-  int job, end;  // job being loaded; end of the worker's job list
+  int job;       // job being loaded
   int stage;     // next stage of that job
   int nst, len, flags;
   const unsigned char* kb;  // K / V address of the next stage's first key, this job's KV head
@@ -286,10 +284,11 @@ __device__ __forceinline__ int issue_stage(const PartialArgs& a, const JobRec* _
   return n;
 }
 
-// The compute side: the job being computed and this wave's share of it.
+// The compute side: the job being computed and this wave's share of it. The job's
+// record itself is read again where it is needed (scalar loads), which keeps the
+// stage loop's scalar registers free.
 struct Work {
-  int job, jj;  // job index; stage within the job
-  JobRec j;
+  int job, nst;          // job index; its stages
   int wr_log, Wk;        // row groups 2^wr_log, key slices Wk
   int rg, ks, nt;        // this wave's row group, key slice, row tiles (<= RTW)
   int tkw, tok_w;        // keys per stage of this wave's slice, and its first key in the stage
@@ -299,25 +298,24 @@ struct Work {
 // Query row of tile `tile`, lane row li, with rows past the last repeating it.
 __device__ __forceinline__ int tile_row(const JobRec& j, int tile, int li) { return min(tile * 16 + li, j.rows - 1); }
 
-// Load job w.job and derive this wave's share.
-__device__ __forceinline__ void open_work(Work& w, const JobRec* __restrict__ jobs, int wave, int g) {
-  w.j = jobs[w.job];
-  w.jj = 0;
+// Start job w.job (record j) and derive this wave's share.
+__device__ __forceinline__ void open_work(Work& w, const JobRec& j, int wave, int g) {
+  w.nst = j.nst;
   // Waves split the row tiles 2^wr_log ways and each stage's keys Wk ways
   // (2^wr_log * Wk <= NW; the other waves only load).
-  w.wr_log = w.j.flags & kJobWrMask;
+  w.wr_log = j.flags & kJobWrMask;
   w.Wk = w.wr_log == 3 ? 1 : 2;
   const int Wr = 1 << w.wr_log;
   w.rg = wave & (Wr - 1);
   w.ks = wave >> w.wr_log;
-  const int ntw = w.ks < w.Wk ? (w.j.tile_n - w.rg + Wr - 1) >> w.wr_log : 0;
+  const int ntw = w.ks < w.Wk ? (j.tile_n - w.rg + Wr - 1) >> w.wr_log : 0;
   w.nt = min(max(ntw, 0), RTW);
   w.tkw = TK / w.Wk;
   w.tok_w = w.ks * w.tkw;
-  const int first = tile_row(w.j, w.j.tile_lo + w.rg, 0);
-  const int last = tile_row(w.j, w.j.tile_lo + w.rg + max(w.nt - 1, 0) * Wr, 15);
-  w.min_lim = min(w.j.lim0 + first / g, w.j.len - 1);
-  w.max_lim = min(w.j.lim0 + last / g, w.j.len - 1);
+  const int first = tile_row(j, j.tile_lo + w.rg, 0);
+  const int last = tile_row(j, j.tile_lo + w.rg + max(w.nt - 1, 0) * Wr, 15);
+  w.min_lim = min(j.lim0 + first / g, j.len - 1);
+  w.max_lim = min(j.lim0 + last / g, j.len - 1);
 }
 
 template <int D>
@@ -331,6 +329,23 @@ struct State {
   float l[RTW];    // this lane's share of the row sum of the fp32 p
   int lim[RTW];    // last visible block key of this lane's row
 };
+
+// Empty accumulators for the next job. Done right after a job's results are stored
+// (not at the next job's first stage), so that the accumulators flow around the stage
+// loop in the same registers.
+template <int D>
+__device__ __forceinline__ void reset(State<D>& st) {
+#pragma unroll
+  for (int t = 0; t < RTW; ++t) {
+#pragma unroll
+    for (int dt = 0; dt < Cfg<D>::DT; ++dt) st.o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m[t] = NEG_INF;
+    st.thr[t] = NEG_INF;
+    st.nmc[t] = 0.f;
+    st.l[t] = 0.f;
+    st.ls[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
 
 // The running reference max m moves only when a row's max exceeds it by more than
 // RESCALE_LOG2 in base 2 (then O and l are rescaled); otherwise p = 2^(s*c - m*c) may
@@ -439,24 +454,24 @@ __device__ __forceinline__ void softmax_step(State<D>& st, int nt, const unsigne
 // 16dt+4G..+3): Cfg<D>::STORES store instructions with every lane active. Lanes of
 // rows past the last query row store that row's values again.
 template <int D>
-__device__ __forceinline__ void write_tile(const State<D>& st, int t, const PartialArgs& a, const Work& w, int tile) {
+__device__ __forceinline__ void write_tile(const State<D>& st, int t, const PartialArgs& a, const JobRec& j, int tile) {
   using C = Cfg<D>;
   const int lane = threadIdx.x & 63;
   const int G = lane >> 4, li = lane & 15;
   const float l = sum4(st.l[t]);
-  const int row = tile_row(w.j, tile, li);
+  const int row = tile_row(j, tile, li);
   const float ls = st.ls[t][0];
   const float inv = ls > 0.f ? 1.f / ls : 0.f;
   const float lse = l > 0.f ? st.m[t] * a.scale + __builtin_amdgcn_logf(l) * LN2 : NEG_INF;
   float* op;
   float* lp;
-  if (a.out != nullptr && (w.j.flags & kJobSingle)) {
+  if (a.out != nullptr && (j.flags & kJobSingle)) {
     const int i = row / a.g, hl = row - i * a.g;
-    const int64_t idx = (w.j.q_tok + i) * a.Hq + w.j.kv * a.g + hl;
+    const int64_t idx = (j.q_tok + i) * a.Hq + j.kv * a.g + hl;
     op = a.out + idx * D;
     lp = a.lse + idx;
   } else {
-    const int64_t prow = w.j.ws_row + row;
+    const int64_t prow = j.ws_row + row;
     op = a.ws_o + prow * D;
     lp = a.ws_lse + prow;
   }
@@ -470,22 +485,22 @@ __device__ __forceinline__ void write_tile(const State<D>& st, int t, const Part
 // DMA only after the following iteration's barrier. Returns the number of store
 // instructions this wave issued.
 template <int D>
-__device__ __forceinline__ int finish_job(State<D>& st, const PartialArgs& a, const Work& w, unsigned char* slot,
-                                          float c) {
+__device__ __forceinline__ int finish_job(State<D>& st, const PartialArgs& a, const Work& w, const JobRec& j,
+                                          unsigned char* slot, float c) {
   using C = Cfg<D>;
   const int lane = threadIdx.x & 63;
   const int Wr = 1 << w.wr_log;
   if (w.Wk == 1) {
 #pragma unroll
     for (int t = 0; t < RTW; ++t)
-      if (t < w.nt) write_tile<D>(st, t, a, w, w.j.tile_lo + w.rg + t * Wr);
+      if (t < w.nt) write_tile<D>(st, t, a, j, j.tile_lo + w.rg + t * Wr);
     return w.nt * C::STORES;
   }
   // Two key slices per row group; one round per tile index (<= Wr records each). The
   // loop is unrolled with compile-time tile indices: a runtime index would put the
   // wave state in scratch memory.
   float* mbuf = reinterpret_cast<float*>(slot);
-  const int rounds = (w.j.tile_n + Wr - 1) >> w.wr_log;
+  const int rounds = (j.tile_n + Wr - 1) >> w.wr_log;
 #pragma unroll
   for (int t = 0; t < RTW; ++t) {
     if (t >= rounds) break;
@@ -518,79 +533,173 @@ __device__ __forceinline__ int finish_job(State<D>& st, const PartialArgs& a, co
             st.o[t][dt][q4] = st.o[t][dt][q4] * a1 + rec[(3 + dt * 4 + q4) * 64 + lane] * a2;
         st.m[t] = ms;
       }
-      write_tile<D>(st, t, a, w, w.j.tile_lo + w.rg + t * Wr);
+      write_tile<D>(st, t, a, j, j.tile_lo + w.rg + t * Wr);
     }
   }
   return w.ks == 0 ? w.nt * C::STORES : 0;
 }
 
-template <int D>
+// Where the workgroup's jobs come from (identical in every wave): first its plan
+// worker's list, up to the start of the shared tail; then, with the queue schedule,
+// chunks of the tail drawn from the sub-queue counters shared by all workgroups.
+struct Feed {
+  int sbeg, send;  // the rest of the static list in wjobs
+  int cbeg, cend;  // the rest of the current chunk
+  int npop;        // pops so far
+  int qk;          // sub-queues found empty (they are tried in turn from this workgroup's own)
+};
+
+// Compute-side queue of the jobs the loader has started (at most three: the stage
+// being computed and two stages in flight can belong to three different jobs).
+struct Started {
+  int j0, j1, j2, n;
+};
+
+__device__ __forceinline__ void started_push(Started& S, int j) {
+  if (S.n == 0)
+    S.j0 = j;
+  else if (S.n == 1)
+    S.j1 = j;
+  else
+    S.j2 = j;
+  ++S.n;
+}
+
+__device__ __forceinline__ void started_pop(Started& S) {
+  S.j0 = S.j1;
+  S.j1 = S.j2;
+  --S.n;
+}
+
+// QUEUE: after its static list, the workgroup draws chunks of the shared tail. A
+// template parameter, so that the static kernel holds no queue code at all.
+template <int D, bool QUEUE>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
-void partial_bf16_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const int32_t* __restrict__ job_ptr) {
+void partial_bf16_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const int32_t* __restrict__ wjobs,
+                         const int32_t* __restrict__ job_ptr, const int32_t* __restrict__ chunk_ptr) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's signature
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDSB];
+  // One LDS object: the pipeline slots, then two words for drawn chunk numbers. (A
+  // separate __shared__ variable makes the compiler wait for the DMA before LDS reads.)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDSB + 16];
+  int* const s_pop = reinterpret_cast<int*>(smem + C::LDSB);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int G = lane >> 4, li = lane & 15;
   const float c = a.scale * LOG2E;
   const float inv_c = 1.f / c;
-
-  const int j_beg = job_ptr[blockIdx.x], j_end = job_ptr[blockIdx.x + 1];
-  if (j_beg >= j_end) return;
+  const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+  constexpr bool queue = QUEUE;
 
   const uint32_t kst = uint32_t(a.k_st) * 2, vst = uint32_t(a.v_st) * 2;  // bytes per token
   LaneOff<D> lo;
   lane_offsets<D>(lo, wave, lane, kst, vst);
 
+  Feed F;
+  F.sbeg = job_ptr[blockIdx.x];
+  F.send = job_ptr[blockIdx.x + 1];
+  F.cbeg = F.cend = 0;
+  F.npop = 0;
+  F.qk = 0;
+
   // Vector-memory instructions this wave issued after the most recent stage's DMA (c1)
   // and after the stage before it (c2).
   int c1 = 0, c2 = 0;
   Loader L;
-  L.job = j_beg;
-  L.end = j_end;
-  open_job(L, a, jobs);
-  bool lmore = true;
-  int issued = 0;
-  int slot_l = 0;  // slot of the next stage to issue
-  for (int k = 0; k < NST - 1 && lmore; ++k) {
-    const int n = issue_stage<D>(a, jobs, L, smem + slot_l * C::SLOTB, lo, wave, lane, kst, vst);
-    c2 = c1 + n;
-    c1 = 0;
-    ++issued;
-    ++slot_l;
-    if (L.stage == L.nst) {
-      lmore = ++L.job < L.end;
-      if (lmore) open_job(L, a, jobs);
+  L.stage = L.nst = 0;  // no job yet
+  int issued = 0, slot_l = 0;
+  Started S;
+  S.n = 0;
+
+  // Next job for the loader, or -1. Drawing a chunk is synchronous: wave 0 waits for
+  // its atomic (only its own few memory operations are older than the wait, it issues
+  // its share of the DMA afterwards) and the workgroup meets at one barrier. Every
+  // wave takes the same branches, so all of them reach that barrier.
+  auto next_job = [&]() -> int {
+    if (F.sbeg < F.send) {
+      const int j = wjobs[__builtin_amdgcn_readfirstlane(F.sbeg)];
+      if (j < a.tail_start) {
+        ++F.sbeg;
+        return j;
+      }
+      F.sbeg = F.send;
     }
-  }
+    if constexpr (queue) {
+      while (F.cbeg == F.cend && F.qk < kQueues) {
+        const int qi = (int(blockIdx.x) + F.qk) % kQueues;
+        if (wave == 0) {
+          if (lane == 0)
+            s_pop[F.npop & 1] = int(__hip_atomic_fetch_add(a.sched + qi * kSchedStride, 1u, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT));
+        }
+        lds_barrier();
+        const int ch = __builtin_amdgcn_readfirstlane(s_pop[F.npop & 1]) * kQueues + qi;
+        ++F.npop;
+        if (ch < a.num_chunks) {
+          F.cbeg = chunk_ptr[ch];
+          F.cend = chunk_ptr[ch + 1];
+        } else {
+          ++F.qk;  // this sub-queue is empty; try the next one
+        }
+      }
+      if (F.cbeg < F.cend) return F.cbeg++;
+    }
+    return -1;
+  };
+  auto ready = [&](int target) {
+    if (issued >= target) return false;
+    if (L.stage < L.nst) return true;
+    const int j = next_job();
+    if (j < 0) return false;
+    L.job = j;
+    open_job(L, a, jobs);
+    started_push(S, j);
+    return true;
+  };
+  // Issue stages until `target` stages are issued or the workgroup has no more jobs.
+  auto loader_step = [&](int target) {
+    while (ready(target)) {
+      const int n = issue_stage<D>(a, jobs, L, smem + slot_l * C::SLOTB, lo, wave, lane, kst, vst);
+      ++issued;
+      slot_l = slot_l == NST - 1 ? 0 : slot_l + 1;
+      c2 = c1 + n;
+      c1 = 0;
+    }
+  };
+
+  loader_step(NST - 1);
 
   Work w;
-  w.job = j_beg;
-  open_work(w, jobs, wave, a.g);
   State<D> st;
+  reset<D>(st);
   int slot_c = 0;  // slot of the stage computed
+  int jj = 0;      // stage within the compute job
   for (int i = 0;; ++i) {
+    if (i >= issued) break;  // the loader is done and every stage computed
     // Stage i landed (for every wave) once the later stages' DMA and the stores after
     // them are all that is pending; stage i + 1, if issued, is the most recent stage.
     wait_stage<D>(issued > i + 1 ? c2 : c1);
     unsigned char* slot = smem + slot_c * C::SLOTB;
 
-    if (w.jj == 0) {
-      // Job start: per-row limits, Q operands, accumulators.
+    if (jj == 0) {
+      // Job start: this wave's share, per-row limits and Q operands.
+      w.job = S.j0;
+      const JobRec j = jobs[w.job];
+      open_work(w, j, wave, a.g);
       const int Wr = 1 << w.wr_log;
 #pragma unroll
       for (int t = 0; t < RTW; ++t) {
-        const int row = tile_row(w.j, w.j.tile_lo + w.rg + t * Wr, li);
-        st.lim[t] = min(w.j.lim0 + row / a.g, w.j.len - 1);
+        const int row = tile_row(j, j.tile_lo + w.rg + t * Wr, li);
+        st.lim[t] = min(j.lim0 + row / a.g, j.len - 1);
       }
-      if (!(w.j.flags & kJobQTile)) {
+      if (!(j.flags & kJobQTile)) {
         // Q from HBM, loaded before this iteration's DMA is issued.
 #pragma unroll
         for (int t = 0; t < RTW; ++t) {
-          const int row = tile_row(w.j, w.j.tile_lo + w.rg + t * Wr, li);
+          const int row = tile_row(j, j.tile_lo + w.rg + t * Wr, li);
           const int iq = row / a.g;
-          const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + (w.j.q_tok + iq) * a.q_st +
-                             int64_t(w.j.kv * a.g + (row - iq * a.g)) * a.q_sh + 8 * G;
+          const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + (j.q_tok + iq) * a.q_st +
+                             int64_t(j.kv * a.g + (row - iq * a.g)) * a.q_sh + 8 * G;
 #pragma unroll
           for (int dc = 0; dc < C::DC; ++dc)
             st.q[t][dc] = t < w.nt ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * dc))
@@ -607,38 +716,18 @@ void partial_bf16_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const i
         // The Q tile of this slot holds rows 0..63 of the job.
 #pragma unroll
         for (int t = 0; t < RTW; ++t) {
-          const int tile = w.j.tile_lo + w.rg + t * Wr;
+          const int tile = j.tile_lo + w.rg + t * Wr;
           const unsigned qa = lds_addr(slot + 2 * C::TILEB) + unsigned(t < w.nt ? tile : 0) * (16 * C::ROWB);
 #pragma unroll
           for (int dc = 0; dc < C::DC; ++dc) st.q[t][dc] = *reinterpret_cast<lds_bf16x8>(uintptr_t(qa + lo.kr[dc]));
         }
       }
-#pragma unroll
-      for (int t = 0; t < RTW; ++t) {
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) st.o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        st.m[t] = NEG_INF;
-        st.thr[t] = NEG_INF;
-        st.nmc[t] = 0.f;
-        st.l[t] = 0.f;
-        st.ls[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
     }
 
-    if (lmore) {
-      const int n = issue_stage<D>(a, jobs, L, smem + slot_l * C::SLOTB, lo, wave, lane, kst, vst);
-      c2 = c1 + n;
-      c1 = 0;
-      ++issued;
-      slot_l = slot_l == NST - 1 ? 0 : slot_l + 1;
-      if (L.stage == L.nst) {
-        lmore = ++L.job < L.end;
-        if (lmore) open_job(L, a, jobs);
-      }
-    }
+    loader_step(i + NST);
 
     // This wave's keys of the stage: block keys [key0, key0 + tkw).
-    const int key0 = w.jj * TK + w.tok_w;
+    const int key0 = jj * TK + w.tok_w;
     if (w.nt > 0 && key0 <= w.max_lim) {
       const bool need_mask = key0 + w.tkw - 1 > w.min_lim;
       const unsigned sb = lds_addr(slot) + unsigned(w.tok_w) * C::ROWB;
@@ -650,29 +739,56 @@ void partial_bf16_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const i
       softmax_step<D, 0>(st, w.nt, ka, va, key0, need_mask, c, inv_c);
       if (w.tkw == TK) softmax_step<D, 32>(st, w.nt, ka, va, key0 + 32, need_mask, c, inv_c);
     }
-    if (w.jj + 1 == w.j.nst) {
-      const int s = finish_job<D>(st, a, w, slot, c);
+    if (jj + 1 == w.nst) {
+      const int s = finish_job<D>(st, a, w, jobs[w.job], slot, c);
       c1 += s;
       c2 += s;
-      if (++w.job >= j_end) break;
-      open_work(w, jobs, wave, a.g);
+      reset<D>(st);
+      started_pop(S);
+      jj = 0;
     } else {
-      ++w.jj;
+      ++jj;
     }
     slot_c = slot_c == NST - 1 ? 0 : slot_c + 1;
   }
+
+  if (threadIdx.x == 0) {
+    if (a.clock != nullptr) {
+      a.clock[2 * blockIdx.x] = t_start;
+      a.clock[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+    }
+    if constexpr (queue) {
+      // The last workgroup to finish (every pop of every workgroup has returned by
+      // then) leaves the queue counters zero for the next launch.
+      uint32_t* const done_ctr = a.sched + kQueues * kSchedStride;
+      const unsigned done = __hip_atomic_fetch_add(done_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (done == gridDim.x - 1) {
+        for (int qi = 0; qi < kQueues; ++qi)
+          __hip_atomic_store(a.sched + qi * kSchedStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(done_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+#endif
 }
 
 }  // namespace
 
 hipError_t launch_partial_bf16(const PartialArgs& a, int head_dim, hipStream_t stream) {
-  dim3 grid(a.num_workers), block(NW * 64);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(partial_bf16_kernel<128>, grid, block, 0, stream, a, a.jobs, a.job_ptr);
-  else if (head_dim == 64)
-    hipLaunchKernelGGL(partial_bf16_kernel<64>, grid, block, 0, stream, a, a.jobs, a.job_ptr);
-  else
+  const dim3 grid(a.num_workers), block(NW * 64);
+  if (head_dim == 128) {
+    if (a.queue)
+      hipLaunchKernelGGL((partial_bf16_kernel<128, true>), grid, block, 0, stream, a, a.jobs, a.wjobs, a.job_ptr, a.chunk_ptr);
+    else
+      hipLaunchKernelGGL((partial_bf16_kernel<128, false>), grid, block, 0, stream, a, a.jobs, a.wjobs, a.job_ptr, a.chunk_ptr);
+  } else if (head_dim == 64) {
+    if (a.queue)
+      hipLaunchKernelGGL((partial_bf16_kernel<64, true>), grid, block, 0, stream, a, a.jobs, a.wjobs, a.job_ptr, a.chunk_ptr);
+    else
+      hipLaunchKernelGGL((partial_bf16_kernel<64, false>), grid, block, 0, stream, a, a.jobs, a.wjobs, a.job_ptr, a.chunk_ptr);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -40,6 +40,7 @@ __global__ __launch_bounds__(256) void partial_f32_kernel(PartialArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const float c = a.scale * LOG2E;
   const int w = blockIdx.x;
+  const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
   const int u0 = a.worker_ptr[w], u1 = a.worker_ptr[w + 1];
   for (int ui = u0; ui < u1; ++ui) {
     const UnitRec u = a.units[ui];
@@ -113,6 +114,10 @@ __global__ __launch_bounds__(256) void partial_f32_kernel(PartialArgs a) {
         __builtin_amdgcn_wave_barrier();
       }
     }
+  }
+  if (a.clock != nullptr && threadIdx.x == 0) {
+    a.clock[2 * w] = t_start;
+    a.clock[2 * w + 1] = __builtin_amdgcn_s_memrealtime();
   }
 }
 

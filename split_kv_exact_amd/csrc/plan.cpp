@@ -193,49 +193,103 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   L.merge_multi_base = off;
   off = align16(off + sizeof(int64_t) * uint64_t(pl->num_multi + 1));
 
-  // Jobs of the bf16 kernel, worker by worker in unit order: for each unit its KV
-  // heads, for each head its row passes.
+  // Jobs of the bf16 kernel in LPT order (units by cost descending, ties in
+  // enumeration order); a unit expands to its KV heads, each head to its row passes.
+  // Each worker's static list holds the jobs of its units in its list order.
   std::vector<JobRec> jobs;
+  std::vector<int32_t> unit_job(n + 1, 0);  // unit u's jobs start at unit_job[u]
+  std::vector<int32_t> unit_njob(n, 0);
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t u = order[i];
+    unit_job[u] = int32_t(jobs.size());
+    const SeqRec& r = pl->seqs[pl->u_seq[u]];
+    const int32_t b = pl->u_block[u];
+    const int64_t key0 = int64_t(b) * B;
+    const int32_t len = pl->u_len[u];
+    // Query token i sees keys up to n - q + i, i.e. block keys t <= (n - q - key0) + i.
+    const int32_t lim0 = pl->causal ? int32_t(std::min<int64_t>(len, r.n - r.q - key0)) : len;
+    const int32_t nrt = (r.rows + 15) / 16;
+    const int32_t kv_lo = per_head ? pl->u_kv[u] : 0, kv_hi = per_head ? kv_lo + 1 : Hkv;
+    for (int32_t kv = kv_lo; kv < kv_hi; ++kv) {
+      for (int32_t t0 = 0; t0 < nrt; t0 += kPassTiles) {
+        JobRec j{};
+        j.kv_tok = r.kv_base + key0;
+        j.q_tok = r.q_base;
+        j.ws_row = r.row_base + (int64_t(kv) * r.nb + b) * r.rows;
+        j.kv = kv;
+        j.len = len;
+        j.lim0 = lim0;
+        j.rows = r.rows;
+        j.tile_lo = t0;
+        j.tile_n = std::min(kPassTiles, nrt - t0);
+        const int32_t rmax = std::min(r.rows, (t0 + j.tile_n) * 16) - 1;
+        const int64_t tmax = std::min<int64_t>(len - 1, int64_t(lim0) + rmax / g);
+        j.nst = tmax < 0 ? 1 : int32_t(tmax / kStageKeys) + 1;
+        const int32_t wr_log = j.tile_n >= 8 ? 3 : j.tile_n >= 4 ? 2 : j.tile_n >= 2 ? 1 : 0;
+        j.flags = wr_log | (r.rows <= kQTileRows ? kJobQTile : 0) | (r.nb == 1 ? kJobSingle : 0);
+        jobs.push_back(j);
+      }
+    }
+    unit_njob[u] = int32_t(jobs.size()) - unit_job[u];
+  }
+  std::vector<int32_t> wjobs;
+  wjobs.reserve(jobs.size());
   std::vector<int32_t> job_ptr(m + 1, 0);
   for (int32_t w = 0; w < m; ++w) {
     for (int32_t i = pl->worker_ptr[w]; i < pl->worker_ptr[w + 1]; ++i) {
       const int32_t u = pl->worker_units[i];
-      const SeqRec& r = pl->seqs[pl->u_seq[u]];
-      const int32_t b = pl->u_block[u];
-      const int64_t key0 = int64_t(b) * B;
-      const int32_t len = pl->u_len[u];
-      // Query token i sees keys up to n - q + i, i.e. block keys t <= (n - q - key0) + i.
-      const int32_t lim0 = pl->causal ? int32_t(std::min<int64_t>(len, r.n - r.q - key0)) : len;
-      const int32_t nrt = (r.rows + 15) / 16;
-      const int32_t kv_lo = per_head ? pl->u_kv[u] : 0, kv_hi = per_head ? kv_lo + 1 : Hkv;
-      for (int32_t kv = kv_lo; kv < kv_hi; ++kv) {
-        for (int32_t t0 = 0; t0 < nrt; t0 += kPassTiles) {
-          JobRec j{};
-          j.kv_tok = r.kv_base + key0;
-          j.q_tok = r.q_base;
-          j.ws_row = r.row_base + (int64_t(kv) * r.nb + b) * r.rows;
-          j.kv = kv;
-          j.len = len;
-          j.lim0 = lim0;
-          j.rows = r.rows;
-          j.tile_lo = t0;
-          j.tile_n = std::min(kPassTiles, nrt - t0);
-          const int32_t rmax = std::min(r.rows, (t0 + j.tile_n) * 16) - 1;
-          const int64_t tmax = std::min<int64_t>(len - 1, int64_t(lim0) + rmax / g);
-          j.nst = tmax < 0 ? 1 : int32_t(tmax / kStageKeys) + 1;
-          const int32_t wr_log = j.tile_n >= 8 ? 3 : j.tile_n >= 4 ? 2 : j.tile_n >= 2 ? 1 : 0;
-          j.flags = wr_log | (r.rows <= kQTileRows ? kJobQTile : 0) | (r.nb == 1 ? kJobSingle : 0);
-          jobs.push_back(j);
-        }
-      }
+      for (int32_t k = 0; k < unit_njob[u]; ++k) wjobs.push_back(unit_job[u] + k);
     }
-    job_ptr[w + 1] = int32_t(jobs.size());
+    job_ptr[w + 1] = int32_t(wjobs.size());
   }
   pl->num_jobs = int64_t(jobs.size());
+  // Queue schedule. Job time is estimated as len * max(rows, 128): a job with few
+  // rows is bound by streaming its block, one with many by the matrix cores. The
+  // jobs at the end of the LPT order that make up the last fifth of the estimated
+  // time form the shared tail, cut into chunks of consecutive jobs of at least
+  // min(half the largest job, 1/32 of a worker's average) estimated time. Chunk c is
+  // entry c / kQueues of sub-queue c % kQueues; workgroup w starts on sub-queue
+  // w % kQueues (workgroups are spread over the XCDs round-robin, so each sub-queue
+  // has one XCD's workgroups as first takers).
+  {
+    const int64_t nj = int64_t(jobs.size());
+    std::vector<int64_t> jc(nj);
+    int64_t total = 0, maxc = 0;
+    for (int64_t i = 0; i < nj; ++i) {
+      const JobRec& j = jobs[i];
+      const int64_t rows = std::min<int64_t>(j.rows, int64_t(j.tile_lo + j.tile_n) * 16) - int64_t(j.tile_lo) * 16;
+      jc[i] = std::max<int64_t>(rows, 128) * j.len;
+      total += jc[i];
+      maxc = std::max(maxc, jc[i]);
+    }
+    int64_t h = nj, acc = 0;
+    while (h > 0 && acc * 5 < total) acc += jc[--h];
+    pl->tail_start = int32_t(h);
+    const int64_t target = std::max<int64_t>(1, std::min(maxc / 2, total / (int64_t(m) * 32)));
+    pl->chunk_ptr.assign(1, int32_t(h));
+    int64_t cur = 0;
+    for (int64_t i = h; i < nj; ++i) {
+      cur += jc[i];
+      if (cur >= target) {
+        pl->chunk_ptr.push_back(int32_t(i + 1));
+        cur = 0;
+      }
+    }
+    if (pl->chunk_ptr.back() != nj) pl->chunk_ptr.push_back(int32_t(nj));
+    // Worth its synchronisation only with many jobs per workgroup.
+    pl->queue_default = nj >= int64_t(24) * m;
+  }
   L.jobs = off;
   off = align16(off + sizeof(JobRec) * jobs.size());
+  L.wjobs = off;
+  off = align16(off + sizeof(int32_t) * std::max<size_t>(wjobs.size(), 1));
   L.job_ptr = off;
   off = align16(off + sizeof(int32_t) * uint64_t(m + 1));
+  L.chunk_ptr = off;
+  off = align16(off + sizeof(int32_t) * pl->chunk_ptr.size());
+  off = (off + 255) & ~uint64_t(255);
+  L.sched = off;
+  off += kSchedBytes;
   L.total = off;
 
   pl->image.assign(L.total, 0);
@@ -266,7 +320,10 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
     }
   }
   if (!jobs.empty()) std::memcpy(base + L.jobs, jobs.data(), sizeof(JobRec) * jobs.size());
+  if (!wjobs.empty()) std::memcpy(base + L.wjobs, wjobs.data(), sizeof(int32_t) * wjobs.size());
   std::memcpy(base + L.job_ptr, job_ptr.data(), sizeof(int32_t) * (m + 1));
+  std::memcpy(base + L.chunk_ptr, pl->chunk_ptr.data(), sizeof(int32_t) * pl->chunk_ptr.size());
+  // The scheduling area (L.sched) stays zero: launches leave it that way.
 }
 
 }  // namespace splitkv

@@ -38,6 +38,14 @@ constexpr int32_t kQTileRows = 64;
 // Row tiles of 16 query rows that one pass of the bf16 kernel covers.
 constexpr int32_t kPassTiles = 16;
 
+// The plan's scheduling area: kQueues uint32 counters of the shared tail's
+// sub-queues (the next entry of each; one per 64-byte line, so that workgroups on
+// different sub-queues do not contend), then the count of finished workgroups. Zero
+// between launches.
+constexpr int32_t kQueues = 8;
+constexpr int32_t kSchedStride = 16;  // uint32 words between counters
+constexpr uint64_t kSchedBytes = 1024;
+
 // Job flags.
 constexpr int32_t kJobWrMask = 3;   // log2 of the row groups the 8 wavefronts form
 constexpr int32_t kJobQTile = 4;    // Q rows of the job travel through LDS with stage 0
@@ -70,8 +78,11 @@ struct ImageLayout {
   uint64_t merge_all;   // int64[S + 1]: prefix of Hkv * rows over all sequences
   uint64_t merge_multi; // int32[S_multi] sequence ids with nb > 1, then
   uint64_t merge_multi_base;  // int64[S_multi + 1]: prefix of Hkv * rows over them
-  uint64_t jobs;        // JobRec[num_jobs], grouped by worker (worker order)
-  uint64_t job_ptr;     // int32[m + 1]: worker w owns jobs [job_ptr[w], job_ptr[w+1])
+  uint64_t jobs;        // JobRec[num_jobs] in LPT order
+  uint64_t wjobs;       // int32[num_jobs]: job indices of each worker's units, worker by worker
+  uint64_t job_ptr;     // int32[m + 1]: worker w's jobs are wjobs[job_ptr[w] .. job_ptr[w+1])
+  uint64_t chunk_ptr;   // int32[num_chunks + 1]: the shared tail's chunks of consecutive jobs
+  uint64_t sched;       // kSchedBytes, 256-byte aligned: counters of the shared job queue
   uint64_t total;
 };
 

@@ -98,10 +98,11 @@ def _plan_handle(lib, d=128):
     return h, inf
 
 
-def _inputs(dtype=L.SPLITKV_BF16, ptr=FAKE, strides=(256, 128, 256, 128, 256, 128), scale=0.0):
+def _inputs(dtype=L.SPLITKV_BF16, ptr=FAKE, strides=(256, 128, 256, 128, 256, 128), scale=0.0,
+            schedule=L.SPLITKV_SCHED_AUTO, clock=None):
     return L.Inputs(q=ptr, k=ptr, v=ptr, q_stride_tok=strides[0], q_stride_head=strides[1],
                     k_stride_tok=strides[2], k_stride_head=strides[3], v_stride_tok=strides[4],
-                    v_stride_head=strides[5], dtype=dtype, scale=scale)
+                    v_stride_head=strides[5], dtype=dtype, scale=scale, schedule=schedule, worker_clock=clock)
 
 
 def test_partial_attn_argument_errors(lib):
@@ -122,6 +123,13 @@ def test_partial_attn_argument_errors(lib):
     assert f(h, dp, ctypes.byref(_inputs(scale=-1.0)), ws, nbytes, None) == L.SPLITKV_ERR_INVALID_ARG
     assert f(h, dp, ctypes.byref(_inputs(scale=float("nan"))), ws, nbytes, None) == L.SPLITKV_ERR_INVALID_ARG
     assert f(h, dp, ctypes.byref(good), None, nbytes, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, dp, ctypes.byref(_inputs(schedule=3)), ws, nbytes, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert b"schedule" in lib.splitkv_last_error()
+    assert f(h, dp, ctypes.byref(_inputs(clock=FAKE + 4)), ws, nbytes, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert b"worker_clock" in lib.splitkv_last_error()
+    big = 1 << 25  # bf16 kernels address a stage with 32-bit offsets: strides above 2^24 are refused
+    assert f(h, dp, ctypes.byref(_inputs(strides=(big, 128, 256, 128, 256, 128))), ws, nbytes,
+             None) == L.SPLITKV_ERR_UNSUPPORTED
     assert f(h, dp, ctypes.byref(good), ws, nbytes - 1, None) == L.SPLITKV_ERR_WORKSPACE
     assert b"workspace needs" in lib.splitkv_last_error()
     lib.splitkv_plan_destroy(h)

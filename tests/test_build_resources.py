@@ -25,8 +25,10 @@ def _hipcc():
 
 
 def _resources(src):
+    from split_kv_exact_amd.build import EXTRA
+
     cmd = [_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", f"-I{ROOT}/include", f"-I{CSRC}",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-x", "hip", "-c",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *EXTRA.get(src, []), "-x", "hip", "-c",
            os.path.join(CSRC, src), "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]

@@ -130,6 +130,49 @@ def test_repeated_calls_reuse_buffers():
         assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
 
 
+def _schedules_agree(wl, q, k, v, m=None):
+    """Partials and fused outputs under every job schedule, bit for bit; afterwards the
+    plan buffer's scheduling area (its last 1024 bytes) is zero again."""
+    plan = skv.plan_for(wl if m is None else wl.with_workers(m))
+    dev_plan = skv.splitkv_plan_upload(plan)
+    res = {}
+    for sched in ("static", "queue", "queue", "auto"):
+        ws = skv.workspace(plan)
+        ws.fill_(float("nan"))
+        skv.splitkv_partial_attn(plan, dev_plan, q, k, v, ws, schedule=sched)
+        out, lse = skv.splitkv_attn(plan, dev_plan, q, k, v, schedule=sched)
+        wo, wlse = skv.workspace_views(plan, ws)
+        res.setdefault(sched, []).append((wo, wlse, out, lse))
+    torch.cuda.synchronize()
+    ref = res["static"][0]
+    assert not torch.isnan(ref[1]).any()
+    for got in res["queue"] + res["auto"]:
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b)
+    assert int(dev_plan[-1024:].count_nonzero()) == 0, "scheduling area not left zero"
+
+
+@pytest.mark.parametrize("wl", [w for w in SMALL if w.dtype == "bfloat16"],
+                         ids=[w.name for w in SMALL if w.dtype == "bfloat16"])
+def test_static_and_queue_schedules_agree(wl):
+    say(f"[gpu] schedules on {wl.name}")
+    q, k, v = make_qkv(wl, "cuda")
+    _schedules_agree(wl, q, k, v)
+
+
+def test_worker_clock():
+    for wl in (SMALL[1], SMALL[0]):  # bf16 and fp32 kernels
+        say(f"[gpu] worker clock on {wl.name}")
+        q, k, v = make_qkv(wl, "cuda")
+        plan = skv.plan_for(wl)
+        dev_plan = skv.splitkv_plan_upload(plan)
+        clock = torch.zeros(2 * wl.num_workers, dtype=torch.int64, device="cuda")
+        skv.splitkv_partial_attn(plan, dev_plan, q, k, v, clock=clock)
+        torch.cuda.synchronize()
+        c = clock.view(-1, 2).cpu()
+        assert bool((c[:, 0] > 0).all()) and bool((c[:, 1] >= c[:, 0]).all())
+
+
 # --------------------------------------------------------------------------- full sizes
 
 def _sample_pairs(rng, wl, s, count):
@@ -242,3 +285,12 @@ def test_full_mixed():
 def test_full_decode_only():
     wl = get_workload("decode")
     _check_sampled(wl, [0, 64, 127], 8)
+
+
+@pytest.mark.parametrize("key", ["batch8", "lognormal", "decode"])
+def test_full_schedules_agree(key):
+    wl = get_workload(key)
+    say(f"[gpu] full-size {wl.name}: static and queue schedules")
+    q, k, v = make_qkv(wl, "cuda")
+    _schedules_agree(wl, q, k, v)
+    del q, k, v
