@@ -74,6 +74,22 @@ def _time_loop(fn, steps, stream, flush=None):
     return tot / steps
 
 
+def _time_each(fn, steps, stream):
+    """Mean milliseconds of fn, each call bracketed by its own pair of HIP events on
+    the stream (kernel time without the gaps between back-to-back launches)."""
+    import torch
+
+    pairs = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        pairs.append((e0, e1))
+    pairs[-1][1].synchronize()
+    return sum(a.elapsed_time(b) for a, b in pairs) / steps
+
+
 def cpu_baseline(wl, q, k, v, budget_s: float):
     """Time the oracle (float64, NumPy) on the host over (sequence, KV head) groups of
     the same workload, in order, until ``budget_s`` seconds of oracle work or the whole
@@ -208,9 +224,10 @@ def main() -> int:
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_wall) * 1e3 / args.steps
 
-    # Dominant kernel (partial attention) and merge, each launched alone, back to back.
-    ms_partial = _time_loop(partial, args.steps, stream)
-    ms_merge = _time_loop(merge, args.steps, stream)
+    # Dominant kernel (partial attention) and merge, each launched alone and timed per
+    # launch: the kernel durations a kernel trace of this run reports.
+    ms_partial = _time_each(partial, args.steps, stream)
+    ms_merge = _time_each(merge, args.steps, stream)
     # Per-step spread: each fused step timed alone (median and minimum).
     per_step = []
     for _ in range(args.steps):

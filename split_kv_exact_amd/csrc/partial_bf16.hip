@@ -353,20 +353,29 @@ __device__ __forceinline__ void reset(State<D>& st) {
 // the same reference, so the result does not depend on when it moved.
 constexpr float RESCALE_LOG2 = 8.f;
 
-// One online-softmax step for this wave: its nt row tiles against 32 keys, block keys
-// key0.. . ka / va are the stage's K / V operand addresses of the wave's first key;
-// the step's keys start KOFF rows later.
-template <int D, int KOFF>
-__device__ __forceinline__ void softmax_step(State<D>& st, int nt, const unsigned (&ka)[Cfg<D>::DC],
-                                             const unsigned (&va)[Cfg<D>::DT], int key0, bool need_mask, float c,
-                                             float inv_c) {
-  using C = Cfg<D>;
-  const int lane = threadIdx.x & 63;
-  const int G = lane >> 4;
+// One online-softmax step of this wave: its nt row tiles against 32 keys (block keys
+// key0..key0+31), in three phases: scores (matrix cores), softmax (vector ALUs),
+// P V (matrix cores). ka / va are the stage's K / V operand addresses of the wave's
+// first key; the step's keys start KOFF rows later. (Interleaving the two steps of a
+// 64-key stage needs more registers than a wave has at two waves per SIMD.)
+constexpr int NT = 2;  // 16-key tiles per step
 
-  // S^T = K Q^T for each 16-key tile, shared K operands across the row tiles.
-  constexpr int NT = 2;
+template <int D>
+struct Scores {
   f32x4 s[RTW][NT];
+};
+
+#ifdef SKV_SETPRIO
+#define SKV_PRIO(x) __builtin_amdgcn_s_setprio(x)
+#else
+#define SKV_PRIO(x) ((void)0)
+#endif
+
+// S^T = K Q^T for each 16-key tile, shared K operands across the row tiles.
+template <int D, int KOFF>
+__device__ __forceinline__ void step_scores(Scores<D>& S, const State<D>& st, int nt, const unsigned (&ka)[Cfg<D>::DC]) {
+  using C = Cfg<D>;
+  SKV_PRIO(1);
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
     bf16x8 kop[C::DC];
@@ -379,12 +388,21 @@ __device__ __forceinline__ void softmax_step(State<D>& st, int nt, const unsigne
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dc = 0; dc < C::DC; ++dc) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[dc], st.q[t][dc], acc, 0, 0, 0);
-        s[t][tt] = acc;
+        S.s[t][tt] = acc;
       }
     }
   }
+  SKV_PRIO(0);
+}
 
-  bf16x4 p[RTW][NT];
+// Mask, running max, p = 2^(s*c - m*c) rounded to bf16 for the P V product; the row
+// sum of the fp32 p goes to l.
+template <int D>
+__device__ __forceinline__ void step_softmax(Scores<D>& S, State<D>& st, int nt, bf16x4 (&p)[RTW][NT], int key0,
+                                             bool need_mask, float c, float inv_c) {
+  using C = Cfg<D>;
+  const int lane = threadIdx.x & 63;
+  const int G = lane >> 4;
 #pragma unroll
   for (int t = 0; t < RTW; ++t) {
     if (t < nt) {
@@ -395,10 +413,10 @@ __device__ __forceinline__ void softmax_step(State<D>& st, int nt, const unsigne
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (16 * tt + e > d) s[t][tt][e] = NEG_INF;
+            if (16 * tt + e > d) S.s[t][tt][e] = NEG_INF;
       }
-      float mx = fmaxf(fmaxf(s[t][0][0], s[t][0][1]), fmaxf(s[t][0][2], s[t][0][3]));
-      mx = fmaxf(mx, fmaxf(fmaxf(s[t][1][0], s[t][1][1]), fmaxf(s[t][1][2], s[t][1][3])));
+      float mx = fmaxf(fmaxf(S.s[t][0][0], S.s[t][0][1]), fmaxf(S.s[t][0][2], S.s[t][0][3]));
+      mx = fmaxf(mx, fmaxf(fmaxf(S.s[t][1][0], S.s[t][1][1]), fmaxf(S.s[t][1][2], S.s[t][1][3])));
       // Move the reference (and rescale) only on a large increase; -inf -> finite always
       // moves. The test first uses this lane's own scores: only when some lane would move
       // is the row max formed across the row's four lanes (rare after the first step).
@@ -420,24 +438,30 @@ __device__ __forceinline__ void softmax_step(State<D>& st, int nt, const unsigne
       for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pe[tt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][tt][e], c, st.nmc[t]));
+          pe[tt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S.s[t][tt][e], c, st.nmc[t]));
           p[t][tt][e] = (__bf16)pe[tt][e];
         }
       st.l[t] += ((pe[0][0] + pe[0][1]) + (pe[0][2] + pe[0][3])) + ((pe[1][0] + pe[1][1]) + (pe[1][2] + pe[1][3]));
     }
   }
+}
 
+// O^T += V^T P^T, and the rounded p summed on the matrix core (an all-ones V^T tile:
+// exact fp32 accumulation, already reduced across lanes). O is normalised by that sum,
+// so it is a convex combination of the values even when one key dominates.
+template <int D, int KOFF>
+__device__ __forceinline__ void step_pv(State<D>& st, int nt, const bf16x4 (&p)[RTW][NT],
+                                        const unsigned (&va)[Cfg<D>::DT]) {
+  using C = Cfg<D>;
   i16x4 lo[C::DT], hi[C::DT];
   tr_read<KOFF * C::ROWB, 16 * C::ROWB>(lo, hi, va);
   bf16x8 vop[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
     vop[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[dt], hi[dt], 0, 1, 2, 3, 4, 5, 6, 7));
-  // An all-ones V^T tile sums the rounded p of each row on the matrix core (exact fp32
-  // accumulation, already reduced across lanes): O is normalised by that sum, so it is a
-  // convex combination of the values even when one key dominates.
   const __bf16 one = (__bf16)1.0f;
   const bf16x8 ones = {one, one, one, one, one, one, one, one};
+  SKV_PRIO(1);
 #pragma unroll
   for (int t = 0; t < RTW; ++t) {
     if (t < nt) {
@@ -447,6 +471,28 @@ __device__ __forceinline__ void softmax_step(State<D>& st, int nt, const unsigne
         st.o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pb, st.o[t][dt], 0, 0, 0);
       st.ls[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, st.ls[t], 0, 0, 0);
     }
+  }
+  SKV_PRIO(0);
+}
+
+// The wave's keys of one stage: 32 keys (one step) or 64 (two steps, interleaved).
+template <int D>
+__device__ __forceinline__ void stage_compute(State<D>& st, int nt, bool two_steps, const unsigned (&ka)[Cfg<D>::DC],
+                                              const unsigned (&va)[Cfg<D>::DT], int key0, bool need_mask, float c,
+                                              float inv_c) {
+  {
+    Scores<D> S;
+    bf16x4 p[RTW][NT];
+    step_scores<D, 0>(S, st, nt, ka);
+    step_softmax<D>(S, st, nt, p, key0, need_mask, c, inv_c);
+    step_pv<D, 0>(st, nt, p, va);
+  }
+  if (two_steps) {
+    Scores<D> S;
+    bf16x4 p[RTW][NT];
+    step_scores<D, 32>(S, st, nt, ka);
+    step_softmax<D>(S, st, nt, p, key0 + 32, need_mask, c, inv_c);
+    step_pv<D, 32>(st, nt, p, va);
   }
 }
 
@@ -736,8 +782,7 @@ void partial_bf16_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const i
       for (int dc = 0; dc < C::DC; ++dc) ka[dc] = sb + lo.kr[dc];
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) va[dt] = sb + C::TILEB + lo.vr[dt];
-      softmax_step<D, 0>(st, w.nt, ka, va, key0, need_mask, c, inv_c);
-      if (w.tkw == TK) softmax_step<D, 32>(st, w.nt, ka, va, key0 + 32, need_mask, c, inv_c);
+      stage_compute<D>(st, w.nt, w.tkw == TK, ka, va, key0, need_mask, c, inv_c);
     }
     if (jj + 1 == w.nst) {
       const int s = finish_job<D>(st, a, w, jobs[w.job], slot, c);
