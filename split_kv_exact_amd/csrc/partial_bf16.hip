@@ -586,7 +586,7 @@ __device__ __forceinline__ int finish_job(State<D>& st, const PartialArgs& a, co
 }
 
 // Where the workgroup's jobs come from (identical in every wave): first its plan
-// worker's list, up to the start of the shared tail; then, with the queue schedule,
+// worker's list without the jobs of the shared tail; then, with the queue schedule,
 // chunks of the tail drawn from the sub-queue counters shared by all workgroups.
 struct Feed {
   int sbeg, send;  // the rest of the static list in wjobs
@@ -662,13 +662,11 @@ void partial_bf16_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const i
   // its share of the DMA afterwards) and the workgroup meets at one barrier. Every
   // wave takes the same branches, so all of them reach that barrier.
   auto next_job = [&]() -> int {
-    if (F.sbeg < F.send) {
+    // Static list; jobs of the shared tail in it are skipped (the tail is drawn below).
+    while (F.sbeg < F.send) {
       const int j = wjobs[__builtin_amdgcn_readfirstlane(F.sbeg)];
-      if (j < a.tail_start) {
-        ++F.sbeg;
-        return j;
-      }
-      F.sbeg = F.send;
+      ++F.sbeg;
+      if (j < a.tail_start) return j;
     }
     if constexpr (queue) {
       while (F.cbeg == F.cend && F.qk < kQueues) {

@@ -232,14 +232,39 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
     }
     unit_njob[u] = int32_t(jobs.size()) - unit_job[u];
   }
+  // Execution order of the static lists. Workgroups are spread over the GPU's 8 XCDs
+  // round-robin (workgroup w on XCD w % 8), and the XCDs have their own L2. A unit with
+  // several jobs (row passes, or KV heads of a whole-block unit) reads its block once
+  // per job, so within each XCD class the jobs of the multi-job units assigned to its
+  // workers are dealt round-robin over those workers, ahead of their single-job units:
+  // a unit's jobs then run at the same time on neighbouring workgroups of one XCD, and
+  // the block is read from HBM about once. Each worker keeps its own single-job units;
+  // the multi-job units of a class are shared evenly by the class.
+  std::vector<std::vector<int32_t>> lists_w(m);
+  const int32_t ncls = (m % 8 == 0 && m >= 16) ? 8 : 1;
+  for (int32_t x = 0; x < ncls; ++x) {
+    std::vector<int32_t> cls;
+    for (int32_t w = x; w < m; w += ncls) cls.push_back(w);
+    std::vector<int32_t> shared;
+    for (int32_t w : cls)
+      for (int32_t i = pl->worker_ptr[w]; i < pl->worker_ptr[w + 1]; ++i) {
+        const int32_t u = pl->worker_units[i];
+        if (unit_njob[u] > 1 && ncls > 1)
+          for (int32_t k = 0; k < unit_njob[u]; ++k) shared.push_back(unit_job[u] + k);
+      }
+    for (size_t k = 0; k < shared.size(); ++k) lists_w[cls[k % cls.size()]].push_back(shared[k]);
+    for (int32_t w : cls)
+      for (int32_t i = pl->worker_ptr[w]; i < pl->worker_ptr[w + 1]; ++i) {
+        const int32_t u = pl->worker_units[i];
+        if (unit_njob[u] == 1 || ncls == 1)
+          for (int32_t k = 0; k < unit_njob[u]; ++k) lists_w[w].push_back(unit_job[u] + k);
+      }
+  }
   std::vector<int32_t> wjobs;
   wjobs.reserve(jobs.size());
   std::vector<int32_t> job_ptr(m + 1, 0);
   for (int32_t w = 0; w < m; ++w) {
-    for (int32_t i = pl->worker_ptr[w]; i < pl->worker_ptr[w + 1]; ++i) {
-      const int32_t u = pl->worker_units[i];
-      for (int32_t k = 0; k < unit_njob[u]; ++k) wjobs.push_back(unit_job[u] + k);
-    }
+    wjobs.insert(wjobs.end(), lists_w[w].begin(), lists_w[w].end());
     job_ptr[w + 1] = int32_t(wjobs.size());
   }
   pl->num_jobs = int64_t(jobs.size());

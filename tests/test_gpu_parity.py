@@ -48,6 +48,9 @@ SMALL = [
     _wl("boosted_keys", [3000, 1500], [16, 1], 64, 8, 128, 512, 32, boost_frac=0.01),
     _wl("many_rows", [2048], [300], 32, 8, 128, 512, 8),
     _wl("more_workers_than_units", [300], [2], 4, 1, 128, 128, 64),
+    # Multi-job units dealt over the workers of an XCD class (needs >= 16 workers).
+    _wl("multi_pass_dealt", [2048, 900, 5000], [300, 70, 16], 32, 8, 128, 512, 32),
+    _wl("whole_block_dealt", [900, 260, 3000], [8, 2, 33], 16, 4, 128, 256, 16, gran=1),
 ]
 
 
