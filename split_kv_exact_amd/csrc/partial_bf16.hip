@@ -228,20 +228,18 @@ __device__ __forceinline__ void open_job(Loader& L, const PartialArgs& a, const 
   L.vb = reinterpret_cast<const unsigned char*>(a.v) + 2 * (j.kv_tok * a.v_st + int64_t(j.kv) * a.v_sh);
 }
 
-// Issue the DMA of the loader's next stage into one pipeline slot and advance the
-// loader; returns the number of vector-memory instructions this wave issued.
-template <int D>
-__device__ __forceinline__ int issue_stage(const PartialArgs& a, const JobRec* __restrict__ jobs, Loader& L,
-                                           unsigned char* slot, const LaneOff<D>& lo, int wave, int lane,
-                                           uint32_t kst, uint32_t vst) {
+// The K and V DMA of one stage with cache policy AUX (0, or 2 = non-temporal).
+template <int D, int AUX>
+__device__ __forceinline__ void issue_kv(const Loader& L, unsigned char* slot, const LaneOff<D>& lo, int wave,
+                                         int lane, uint32_t kst, uint32_t vst) {
   using C = Cfg<D>;
   const int rem = L.len - L.stage * TK;  // keys of the block from this stage's first key on
   if (rem >= TK) {
 #pragma unroll
     for (int in = 0; in < C::KV_INST; ++in) {
       const int gi = wave * C::KV_INST + in;
-      __builtin_amdgcn_global_load_lds(L.kb + lo.dk[in], (lds_void*)(slot + gi * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(L.vb + lo.dv[in], (lds_void*)(slot + C::TILEB + gi * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(L.kb + lo.dk[in], (lds_void*)(slot + gi * 1024), 16, 0, AUX);
+      __builtin_amdgcn_global_load_lds(L.vb + lo.dv[in], (lds_void*)(slot + C::TILEB + gi * 1024), 16, 0, AUX);
     }
   } else {
     // The block ends inside this stage: rows past its end re-read its last key (finite
@@ -253,11 +251,24 @@ __device__ __forceinline__ int issue_stage(const PartialArgs& a, const JobRec* _
       const int row = gi * C::RPI + lane / C::CH;
       const uint32_t t = uint32_t(min(row, rem - 1));
       __builtin_amdgcn_global_load_lds(L.kb + (t * kst + 16u * swz_k<D>(row, cs)), (lds_void*)(slot + gi * 1024),
-                                       16, 0, 0);
+                                       16, 0, AUX);
       __builtin_amdgcn_global_load_lds(L.vb + (t * vst + 16u * swz_v<D>(row, cs)),
-                                       (lds_void*)(slot + C::TILEB + gi * 1024), 16, 0, 0);
+                                       (lds_void*)(slot + C::TILEB + gi * 1024), 16, 0, AUX);
     }
   }
+}
+
+// Issue the DMA of the loader's next stage into one pipeline slot and advance the
+// loader; returns the number of vector-memory instructions this wave issued.
+template <int D>
+__device__ __forceinline__ int issue_stage(const PartialArgs& a, const JobRec* __restrict__ jobs, Loader& L,
+                                           unsigned char* slot, const LaneOff<D>& lo, int wave, int lane,
+                                           uint32_t kst, uint32_t vst) {
+  using C = Cfg<D>;
+  if (L.flags & kJobStream)
+    issue_kv<D, 2>(L, slot, lo, wave, lane, kst, vst);
+  else
+    issue_kv<D, 0>(L, slot, lo, wave, lane, kst, vst);
   int n = 2 * C::KV_INST;
   if (L.stage == 0 && (L.flags & kJobQTile)) {
     // The job's query rows (at most 64) ride with its first stage; rows past the last

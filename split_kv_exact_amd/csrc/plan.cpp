@@ -242,6 +242,12 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   // the multi-job units of a class are shared evenly by the class.
   std::vector<std::vector<int32_t>> lists_w(m);
   const int32_t ncls = (m % 8 == 0 && m >= 16) ? 8 : 1;
+  // A block read by one job, or by jobs dealt to distinct workers of one class (which
+  // read it at about the same time), is not read again afterwards: its K/V loads carry
+  // the non-temporal hint, so the streamed lines do not displace reused ones in L2.
+  for (int64_t u = 0; u < n; ++u)
+    if (unit_njob[u] == 1 || (ncls > 1 && unit_njob[u] <= m / ncls))
+      for (int32_t k = 0; k < unit_njob[u]; ++k) jobs[unit_job[u] + k].flags |= kJobStream;
   for (int32_t x = 0; x < ncls; ++x) {
     std::vector<int32_t> cls;
     for (int32_t w = x; w < m; w += ncls) cls.push_back(w);

@@ -50,6 +50,7 @@ constexpr uint64_t kSchedBytes = 1024;
 constexpr int32_t kJobWrMask = 3;   // log2 of the row groups the 8 wavefronts form
 constexpr int32_t kJobQTile = 4;    // Q rows of the job travel through LDS with stage 0
 constexpr int32_t kJobSingle = 8;   // the sequence has a single block (its result is final)
+constexpr int32_t kJobStream = 16;  // K/V read with the non-temporal hint (the block is not read again later)
 
 // One job of the bf16 partial-attention kernel: one pass over a block's keys for one
 // KV head and up to kPassTiles row tiles of its query rows. Query row r of a KV head
