@@ -154,6 +154,9 @@ def main() -> int:
     ap.add_argument("--no-flush", action="store_true", help="skip the cold-cache per-step measurement")
     ap.add_argument("--schedule", default="auto", choices=("auto", "queue", "static"),
                     help="how the partial-attention workgroups take their jobs (bf16)")
+    ap.add_argument("--cost-ridge", type=int, default=0,
+                    help="LPT unit cost: 0 = q * len * heads (the pages' cost); R > 0 = len * max(q * g, R) "
+                         "per KV head (roofline-aware, R = ridge in query rows)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (a kernel of known traffic, for scaling "
                          "hardware byte counters)")
@@ -183,7 +186,7 @@ def main() -> int:
     plan_times = []
     for _ in range(20):
         t0 = time.perf_counter_ns()
-        plan = skv.plan_for(wl)
+        plan = skv.plan_for(wl, args.cost_ridge)
         plan_times.append((time.perf_counter_ns() - t0) / 1e6)
     plan_times.sort()
     info = plan.info()
@@ -250,6 +253,9 @@ def main() -> int:
         "busy_us_max": round(float(busy.max()), 2),
         "imbalance": round(float(busy.max() / busy.mean() - 1.0), 4),
         "end_spread_us": round(float((ck[:, 1].max() - ck[:, 1].min()) / 100.0), 2),
+        # Workgroups are dealt to the 8 XCDs round-robin (workgroup w on XCD w % 8).
+        "busy_us_mean_by_xcd": [round(float(busy[x::8].mean()), 1) for x in range(8)]
+        if wl.num_workers % 8 == 0 else None,
     }
     ms_cold = None
     if not args.no_flush:
@@ -308,6 +314,7 @@ def main() -> int:
         "lpt": {
             "units": info["num_units"],
             "workers": wl.num_workers,
+            "cost_ridge_rows": args.cost_ridge,
             "imbalance": info["imbalance"],
             "makespan": info["makespan"],
             "lower_bound": info["lower_bound"],

@@ -52,7 +52,7 @@ extern "C" {
 #endif
 
 #define SPLITKV_VERSION_MAJOR 0
-#define SPLITKV_VERSION_MINOR 2
+#define SPLITKV_VERSION_MINOR 3
 
 typedef enum {
   SPLITKV_OK = 0,
@@ -102,13 +102,18 @@ typedef struct {
   int32_t num_workers;      /* m >= 1 LPT workers = workgroups of the attention launch */
   int32_t causal;           /* 1: bottom-right causal mask on the trailing queries   */
   int32_t granularity;      /* splitkv_granularity                                   */
+  int32_t cost_ridge_rows;  /* R >= 0, the unit cost model (see splitkv_plan):          *
+                             * 0 = the Split-KV page's q_s * len * heads;              *
+                             * R > 0 = len * max(q_s * g, R) per KV head, i.e. a unit  *
+                             * served by fewer than R query rows per KV head costs as  *
+                             * streaming its block does (roofline-aware cost)          */
 } splitkv_problem;
 
 typedef struct splitkv_plan_s splitkv_plan_t; /* opaque, library-owned host object */
 
 typedef struct {
   int64_t num_units;      /* LPT units                                                 */
-  int64_t total_cost;     /* sum of unit costs q_s * len * heads                       */
+  int64_t total_cost;     /* sum of unit costs (the cost model of splitkv_problem)     */
   int64_t makespan;       /* largest worker load                                       */
   int64_t lower_bound;    /* max(ceil(total/m), largest unit cost)                     */
   double imbalance;       /* (m * makespan - total) / total, one float64 division      */
@@ -144,11 +149,19 @@ int splitkv_version(void);
 
 /* Build the LPT plan on the host (no HIP call). Split-KV page, "Timeline": context KV
  * blocks are allocated by a cost-aware LPT. Units are enumerated (seq, block, kv head)
- * lexicographically, cost = q_s * len * heads served, stable sort by cost descending,
- * each unit to the least-loaded worker (ties to the lowest index). On success *out is
- * a new plan the caller releases with splitkv_plan_destroy.
+ * lexicographically, stable sort by cost descending, each unit to the least-loaded
+ * worker (ties to the lowest index). The cost of a unit serving heads query heads
+ * (g per KV head, or Hq for a whole block) is, with R = cost_ridge_rows,
+ *   R = 0:  q_s * len * heads                      (the page's cost: Lq x length x heads)
+ *   R > 0:  len * max(q_s * g, R) * (heads / g)    (a block of one KV head is read in
+ *           time ~ len and its q_s * g rows computed in time ~ len * rows / R, so R is
+ *           the machine's ridge in query rows: its flop/byte ratio times the bytes per
+ *           key over the flops per key and row; 312 for bf16 at MI355X's published
+ *           peaks, about 128 for the attention kernels of this library as measured)
+ * R = 0 and q_s * g >= R give the same cost. On success *out is a new plan the caller
+ * releases with splitkv_plan_destroy.
  * Errors: INVALID_ARG (null pointers, S < 1, q_s < 1, n_s < q_s, Hq % Hkv != 0,
- * B < 1, m < 1, bad granularity), ALLOC. */
+ * B < 1, m < 1, bad granularity, R < 0 or R > 2^30, total cost beyond 2^62), ALLOC. */
 int splitkv_plan(const splitkv_problem *problem, splitkv_plan_t **out);
 
 /* Plan statistics and buffer sizes. Errors: INVALID_ARG. */

@@ -11,6 +11,13 @@ nor the tie-breaks nor the definition of the rate; the readings here are:
 * Cost: q_s * len_b * heads, where heads is the number of query heads the unit
   serves (g = Hq/Hkv for a per-KV-head unit; Hq when a unit is a whole
   (sequence, block) pair, the coarser granularity). Integer arithmetic.
+* Roofline-aware cost (an alternative the pages do not give; their cost counts
+  query rows only, so a block read for a single query row looks nearly free):
+  with a ridge of R query rows per KV head, a unit costs len_b * max(q_s * g, R)
+  for each KV head it covers. Its block is streamed in time proportional to len_b
+  whatever the rows, and its scores take time proportional to len_b * rows once
+  the rows exceed the machine's flop-per-byte ratio, expressed in rows (R). R = 0
+  is the pages' cost again.
 * LPT (Graham): take units by cost, largest first, ties in enumeration order
   (a stable sort); give each to the worker with the least load so far, ties to the
   lowest worker index. A worker's units are kept in the order they were given.
@@ -36,8 +43,12 @@ def enumerate_units(
     num_kv_heads: int,
     block_len: int,
     granularity: int = UNIT_SEQ_BLOCK_KVHEAD,
+    ridge_rows: int = 0,
 ) -> List[Tuple[int, int, int, int, int]]:
-    """Units as (seq, block, kv_head, length, cost); kv_head = -1 for whole-block units."""
+    """Units as (seq, block, kv_head, length, cost); kv_head = -1 for whole-block units.
+
+    ridge_rows = 0 gives the pages' cost, q * length * heads; ridge_rows = R > 0 the
+    roofline-aware length * max(q * g, R) per KV head covered."""
     g = num_q_heads // num_kv_heads
     units = []
     for s, (n, q) in enumerate(zip(kv_lens, q_lens)):
@@ -45,11 +56,15 @@ def enumerate_units(
         nb = -(-n // block_len)
         for b in range(nb):
             length = min(block_len, n - b * block_len)
+            if ridge_rows == 0:
+                per_kv = q * length * g
+            else:
+                per_kv = length * max(q * g, ridge_rows)
             if granularity == UNIT_SEQ_BLOCK_KVHEAD:
                 for kappa in range(num_kv_heads):
-                    units.append((s, b, kappa, length, q * length * g))
+                    units.append((s, b, kappa, length, per_kv))
             else:
-                units.append((s, b, -1, length, q * length * num_q_heads))
+                units.append((s, b, -1, length, per_kv * num_kv_heads))
     return units
 
 
@@ -88,9 +103,10 @@ def plan_ref(
     block_len: int,
     num_workers: int,
     granularity: int = UNIT_SEQ_BLOCK_KVHEAD,
+    ridge_rows: int = 0,
 ) -> Dict[str, object]:
     """The whole plan: units, assignment, CSR lists, loads, makespan and imbalance."""
-    units = enumerate_units(kv_lens, q_lens, num_q_heads, num_kv_heads, block_len, granularity)
+    units = enumerate_units(kv_lens, q_lens, num_q_heads, num_kv_heads, block_len, granularity, ridge_rows)
     costs = [u[4] for u in units]
     worker_of, lists, loads = lpt_ref(costs, num_workers)
     ptr = [0]

@@ -57,6 +57,7 @@ class Problem(ctypes.Structure):
         ("num_workers", ctypes.c_int32),
         ("causal", ctypes.c_int32),
         ("granularity", ctypes.c_int32),
+        ("cost_ridge_rows", ctypes.c_int32),
     ]
 
 

@@ -85,8 +85,10 @@ def splitkv_plan(
     num_workers: int,
     causal: bool = True,
     granularity: int = L.SPLITKV_UNIT_SEQ_BLOCK_KVHEAD,
+    cost_ridge_rows: int = 0,
 ) -> Plan:
-    """Build the LPT plan on the host (``splitkv_plan``)."""
+    """Build the LPT plan on the host (``splitkv_plan``). ``cost_ridge_rows`` selects the
+    unit cost: 0 is q * len * heads, R > 0 is len * max(q * g, R) per KV head."""
     lib = L.load()
     kv = np.ascontiguousarray(np.asarray(kv_lens, dtype=np.int64))
     ql = np.ascontiguousarray(np.asarray(q_lens, dtype=np.int32))
@@ -101,19 +103,20 @@ def splitkv_plan(
         num_workers=num_workers,
         causal=int(bool(causal)),
         granularity=granularity,
+        cost_ridge_rows=cost_ridge_rows,
     )
     h = ctypes.c_void_p()
     _check(lib, lib.splitkv_plan(ctypes.byref(prob), ctypes.byref(h)), "splitkv_plan")
     problem = dict(kv_lens=kv.tolist(), q_lens=ql.tolist(), num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                    head_dim=head_dim, block_len=block_len, num_workers=num_workers, causal=bool(causal),
-                   granularity=granularity)
+                   granularity=granularity, cost_ridge_rows=cost_ridge_rows)
     return Plan(h, problem, lib)
 
 
-def plan_for(wl) -> Plan:
+def plan_for(wl, cost_ridge_rows: int = 0) -> Plan:
     """Plan for a ``workloads.Workload``."""
     return splitkv_plan(wl.kv_lens, wl.q_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_len,
-                        wl.num_workers, wl.causal, wl.granularity)
+                        wl.num_workers, wl.causal, wl.granularity, cost_ridge_rows)
 
 
 # --------------------------------------------------------------------------- device side

@@ -5,7 +5,8 @@
 // The page gives no cost model, tie-break or imbalance definition; this planner uses
 //   unit       = (sequence, block, KV head), enumerated in that order (or a whole
 //                (sequence, block) serving every query head: the coarse granularity);
-//   cost       = q_s * block length * query heads served (exact int64);
+//   cost       = q_s * block length * query heads served (exact int64), or with a
+//                ridge R > 0 the roofline-aware len * max(q_s * g, R) per KV head;
 //   order      = costs descending, ties in enumeration order (stable sort);
 //   placement  = worker with the smallest (load, index) via a binary min-heap;
 //   imbalance  = (m * max_load - total) / total, one float64 division.
@@ -39,6 +40,7 @@ bool validate_problem(const splitkv_problem* p, std::string* why) {
   if (p->causal != 0 && p->causal != 1) return fail("causal must be 0 or 1");
   if (p->granularity != SPLITKV_UNIT_SEQ_BLOCK_KVHEAD && p->granularity != SPLITKV_UNIT_SEQ_BLOCK)
     return fail("unknown granularity");
+  if (p->cost_ridge_rows < 0 || p->cost_ridge_rows > (1 << 30)) return fail("cost_ridge_rows must be in [0, 2^30]");
   const int64_t g = p->num_q_heads / p->num_kv_heads;
   for (int32_t s = 0; s < p->batch; ++s) {
     if (p->q_lens[s] < 1) return fail("every q_len must be >= 1");
@@ -47,6 +49,13 @@ bool validate_problem(const splitkv_problem* p, std::string* why) {
     // Keep per-unit row counts in int32 and per-unit costs far from int64 overflow.
     if (int64_t(p->q_lens[s]) * g > (int64_t(1) << 30)) return fail("q_len * group too large");
   }
+  // Every unit cost and their sum must stay exact in int64: bound the sum, per
+  // sequence len * max(q * g, R) * Hkv over its n_s keys, in floating point.
+  double total = 0.0;
+  for (int32_t s = 0; s < p->batch; ++s)
+    total += double(p->kv_lens[s]) * double(std::max<int64_t>(int64_t(p->q_lens[s]) * g, p->cost_ridge_rows)) *
+             double(p->num_kv_heads);
+  if (total > 4.0e18) return fail("total unit cost beyond 2^62");
   return true;
 }
 
@@ -59,6 +68,7 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   pl->m = p->num_workers;
   pl->causal = p->causal;
   pl->granularity = p->granularity;
+  pl->ridge = p->cost_ridge_rows;
   pl->g = p->num_q_heads / p->num_kv_heads;
   pl->kv_lens.assign(p->kv_lens, p->kv_lens + p->batch);
   pl->q_lens.assign(p->q_lens, p->q_lens + p->batch);
@@ -110,7 +120,10 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
     const SeqRec& r = pl->seqs[s];
     for (int32_t b = 0; b < r.nb; ++b) {
       const int32_t len = int32_t(std::min<int64_t>(B, r.n - int64_t(b) * B));
-      const int64_t cost = int64_t(r.q) * len * heads;
+      // heads = g per KV-head unit or Hq = g * Hkv per whole-block unit.
+      const int64_t rows = int64_t(r.q) * g;
+      const int64_t cost = pl->ridge == 0 ? int64_t(r.q) * len * heads
+                                          : int64_t(len) * std::max<int64_t>(rows, pl->ridge) * (heads / g);
       if (per_head) {
         for (int32_t k = 0; k < Hkv; ++k) {
           pl->u_seq.push_back(s);

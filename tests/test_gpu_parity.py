@@ -134,25 +134,29 @@ def test_repeated_calls_reuse_buffers():
 
 
 def _schedules_agree(wl, q, k, v, m=None):
-    """Partials and fused outputs under every job schedule, bit for bit; afterwards the
-    plan buffer's scheduling area (its last 1024 bytes) is zero again."""
-    plan = skv.plan_for(wl if m is None else wl.with_workers(m))
-    dev_plan = skv.splitkv_plan_upload(plan)
+    """Partials and fused outputs under every job schedule, and under a plan built with
+    the roofline-aware cost (other placement, same jobs), bit for bit; afterwards the
+    plan buffers' scheduling areas (their last 1024 bytes) are zero again."""
+    w = wl if m is None else wl.with_workers(m)
     res = {}
-    for sched in ("static", "queue", "queue", "auto"):
-        ws = skv.workspace(plan)
-        ws.fill_(float("nan"))
-        skv.splitkv_partial_attn(plan, dev_plan, q, k, v, ws, schedule=sched)
-        out, lse = skv.splitkv_attn(plan, dev_plan, q, k, v, schedule=sched)
-        wo, wlse = skv.workspace_views(plan, ws)
-        res.setdefault(sched, []).append((wo, wlse, out, lse))
-    torch.cuda.synchronize()
-    ref = res["static"][0]
+    for ridge, scheds in ((0, ("static", "queue", "queue", "auto")), (128, ("static", "queue"))):
+        plan = skv.plan_for(w, ridge)
+        dev_plan = skv.splitkv_plan_upload(plan)
+        for sched in scheds:
+            ws = skv.workspace(plan)
+            ws.fill_(float("nan"))
+            skv.splitkv_partial_attn(plan, dev_plan, q, k, v, ws, schedule=sched)
+            out, lse = skv.splitkv_attn(plan, dev_plan, q, k, v, schedule=sched)
+            wo, wlse = skv.workspace_views(plan, ws)
+            res.setdefault((ridge, sched), []).append((wo, wlse, out, lse))
+        torch.cuda.synchronize()
+        assert int(dev_plan[-1024:].count_nonzero()) == 0, "scheduling area not left zero"
+    ref = res[(0, "static")][0]
     assert not torch.isnan(ref[1]).any()
-    for got in res["queue"] + res["auto"]:
-        for a, b in zip(got, ref):
-            assert torch.equal(a, b)
-    assert int(dev_plan[-1024:].count_nonzero()) == 0, "scheduling area not left zero"
+    for key, runs in res.items():
+        for got in runs:
+            for a, b in zip(got, ref):
+                assert torch.equal(a, b), key
 
 
 @pytest.mark.parametrize("wl", [w for w in SMALL if w.dtype == "bfloat16"],

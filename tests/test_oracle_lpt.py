@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 from oracle import enumerate_units, imbalance_ref, lpt_ref, opt_exhaustive, plan_ref
+from oracle.lpt import UNIT_SEQ_BLOCK, UNIT_SEQ_BLOCK_KVHEAD
 from tests.golden_io import read_graham, read_plans
 from workloads import get_workload
 
@@ -109,3 +110,27 @@ def test_every_unit_assigned_once_and_lists_in_assignment_order():
         assert sum(costs[u] for u in lst) == loads[w]
         # a worker receives units in non-increasing cost order (LPT order)
         assert all(costs[a] >= costs[b] for a, b in zip(lst, lst[1:]))
+
+
+def test_roofline_cost_worked_example():
+    """Roofline-aware unit costs, computed by hand.
+
+    Two sequences, Hq = 8 over Hkv = 2 (g = 4), B = 4096, ridge R = 128 rows:
+      seq 0: n = 5000, q = 2 -> 8 rows per KV head, blocks of 4096 and 904 keys:
+             4096 * max(8, 128) = 524288 and 904 * 128 = 115712 per KV head;
+      seq 1: n = 300, q = 40 -> 160 rows, one block: 300 * 160 = 48000 (rows above
+             R, so the same as the pages' cost 40 * 300 * 4).
+    The pages' costs of seq 0's blocks would be 2 * 4096 * 4 = 32768 and 7232.
+    """
+    units = enumerate_units([5000, 300], [2, 40], 8, 2, 4096, UNIT_SEQ_BLOCK_KVHEAD, 128)
+    assert [u[4] for u in units] == [524288, 524288, 115712, 115712, 48000, 48000]
+    assert [u[3] for u in units] == [4096, 4096, 904, 904, 300, 300]
+    whole = enumerate_units([5000, 300], [2, 40], 8, 2, 4096, UNIT_SEQ_BLOCK, 128)
+    assert [u[4] for u in whole] == [1048576, 231424, 96000]
+    pages = enumerate_units([5000, 300], [2, 40], 8, 2, 4096, UNIT_SEQ_BLOCK_KVHEAD, 0)
+    assert [u[4] for u in pages] == [32768, 32768, 7232, 7232, 48000, 48000]
+    # LPT on two workers: 524288 each, then 115712 each, then 48000 each.
+    plan = plan_ref([5000, 300], [2, 40], 8, 2, 4096, 2, UNIT_SEQ_BLOCK_KVHEAD, 128)
+    assert plan["loads"] == [688000, 688000]
+    assert plan["worker_units"] == [0, 2, 4, 1, 3, 5]
+    assert plan["imbalance"] == 0.0

@@ -8,11 +8,11 @@ from split_kv_exact_amd import splitkv_plan
 from workloads import WORKLOADS, get_workload
 
 
-def compare(kv, q, hq, hkv, b, m, gran=0, d=128):
-    pl = splitkv_plan(kv, q, hq, hkv, d, b, m, True, gran)
+def compare(kv, q, hq, hkv, b, m, gran=0, d=128, ridge=0):
+    pl = splitkv_plan(kv, q, hq, hkv, d, b, m, True, gran, ridge)
     ex = pl.export()
     inf = pl.info()
-    ref = plan_ref(kv, q, hq, hkv, b, m, gran)
+    ref = plan_ref(kv, q, hq, hkv, b, m, gran, ridge)
     units = ref["units"]
     assert inf["num_units"] == len(units)
     assert ex["unit_seq"].tolist() == [u[0] for u in units]
@@ -34,10 +34,11 @@ def compare(kv, q, hq, hkv, b, m, gran=0, d=128):
 
 @pytest.mark.parametrize("key", sorted(WORKLOADS))
 @pytest.mark.parametrize("gran", [0, 1])
-def test_workload_plans_bit_exact(key, gran):
+@pytest.mark.parametrize("ridge", [0, 128, 312])
+def test_workload_plans_bit_exact(key, gran, ridge):
     wl = get_workload(key)
     compare(wl.kv_lens, wl.q_lens, wl.num_q_heads, wl.num_kv_heads, wl.block_len, wl.num_workers, gran,
-            wl.head_dim)
+            wl.head_dim, ridge)
 
 
 def test_random_instances_bit_exact():
@@ -51,7 +52,7 @@ def test_random_instances_bit_exact():
         kv = [int(x) for x in rng.integers(1, 3000, size=S)]
         q = [int(rng.integers(1, k + 1)) for k in kv]
         q = [min(x, 50) for x in q]
-        compare(kv, q, g * hkv, hkv, b, m, int(rng.integers(0, 2)))
+        compare(kv, q, g * hkv, hkv, b, m, int(rng.integers(0, 2)), ridge=int(rng.choice([0, 1, 7, 128])))
 
 
 def test_worker_count_larger_than_units():
