@@ -245,14 +245,27 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
     }
     unit_njob[u] = int32_t(jobs.size()) - unit_job[u];
   }
+  // Estimated job time, len * max(rows, 128): a job with few rows is bound by streaming
+  // its block, one with many by the matrix cores.
+  const int64_t nj = int64_t(jobs.size());
+  std::vector<int64_t> jc(nj);
+  int64_t jc_total = 0, jc_max = 0;
+  for (int64_t i = 0; i < nj; ++i) {
+    const JobRec& j = jobs[i];
+    const int64_t rows = std::min<int64_t>(j.rows, int64_t(j.tile_lo + j.tile_n) * 16) - int64_t(j.tile_lo) * 16;
+    jc[i] = std::max<int64_t>(rows, 128) * j.len;
+    jc_total += jc[i];
+    jc_max = std::max(jc_max, jc[i]);
+  }
   // Execution order of the static lists. Workgroups are spread over the GPU's 8 XCDs
   // round-robin (workgroup w on XCD w % 8), and the XCDs have their own L2. A unit with
   // several jobs (row passes, or KV heads of a whole-block unit) reads its block once
-  // per job, so within each XCD class the jobs of the multi-job units assigned to its
-  // workers are dealt round-robin over those workers, ahead of their single-job units:
-  // a unit's jobs then run at the same time on neighbouring workgroups of one XCD, and
-  // the block is read from HBM about once. Each worker keeps its own single-job units;
-  // the multi-job units of a class are shared evenly by the class.
+  // per job, so within each XCD class (workers w = x mod 8) the jobs of the multi-job
+  // units assigned to its workers are shared by the class: taken in LPT order, each
+  // goes to the class worker with the least estimated time so far (its own single-job
+  // units counted first), and runs ahead of that worker's single-job units. A unit's
+  // jobs then run at the same time on neighbouring workgroups of one XCD, and the block
+  // is read from HBM about once; the class's workers stay balanced in estimated time.
   std::vector<std::vector<int32_t>> lists_w(m);
   const int32_t ncls = (m % 8 == 0 && m >= 16) ? 8 : 1;
   // A block read by one job, or by jobs dealt to distinct workers of one class (which
@@ -262,17 +275,31 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
     if (unit_njob[u] == 1 || (ncls > 1 && unit_njob[u] <= m / ncls))
       for (int32_t k = 0; k < unit_njob[u]; ++k) jobs[unit_job[u] + k].flags |= kJobStream;
   for (int32_t x = 0; x < ncls; ++x) {
-    std::vector<int32_t> cls;
-    for (int32_t w = x; w < m; w += ncls) cls.push_back(w);
     std::vector<int32_t> shared;
-    for (int32_t w : cls)
+    typedef std::pair<int64_t, int32_t> LoadW;  // (estimated time, worker)
+    std::priority_queue<LoadW, std::vector<LoadW>, std::greater<LoadW>> heap;
+    for (int32_t w = x; w < m; w += ncls) {
+      int64_t own = 0;
       for (int32_t i = pl->worker_ptr[w]; i < pl->worker_ptr[w + 1]; ++i) {
         const int32_t u = pl->worker_units[i];
-        if (unit_njob[u] > 1 && ncls > 1)
-          for (int32_t k = 0; k < unit_njob[u]; ++k) shared.push_back(unit_job[u] + k);
+        for (int32_t k = 0; k < unit_njob[u]; ++k) {
+          if (unit_njob[u] > 1 && ncls > 1)
+            shared.push_back(unit_job[u] + k);
+          else
+            own += jc[unit_job[u] + k];
+        }
       }
-    for (size_t k = 0; k < shared.size(); ++k) lists_w[cls[k % cls.size()]].push_back(shared[k]);
-    for (int32_t w : cls)
+      heap.push(LoadW(own, w));
+    }
+    std::sort(shared.begin(), shared.end());  // job numbers follow the LPT order
+    for (int32_t jn : shared) {
+      LoadW e = heap.top();
+      heap.pop();
+      lists_w[e.second].push_back(jn);
+      e.first += jc[jn];
+      heap.push(e);
+    }
+    for (int32_t w = x; w < m; w += ncls)
       for (int32_t i = pl->worker_ptr[w]; i < pl->worker_ptr[w + 1]; ++i) {
         const int32_t u = pl->worker_units[i];
         if (unit_njob[u] == 1 || ncls == 1)
@@ -287,25 +314,14 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
     job_ptr[w + 1] = int32_t(wjobs.size());
   }
   pl->num_jobs = int64_t(jobs.size());
-  // Queue schedule. Job time is estimated as len * max(rows, 128): a job with few
-  // rows is bound by streaming its block, one with many by the matrix cores. The
-  // jobs at the end of the LPT order that make up the last fifth of the estimated
-  // time form the shared tail, cut into chunks of consecutive jobs of at least
-  // min(half the largest job, 1/32 of a worker's average) estimated time. Chunk c is
-  // entry c / kQueues of sub-queue c % kQueues; workgroup w starts on sub-queue
-  // w % kQueues (workgroups are spread over the XCDs round-robin, so each sub-queue
-  // has one XCD's workgroups as first takers).
+  // Queue schedule. The jobs at the end of the LPT order that make up the last fifth
+  // of the estimated time form the shared tail, cut into chunks of consecutive jobs of
+  // at least min(half the largest job, 1/32 of a worker's average) estimated time.
+  // Chunk c is entry c / kQueues of sub-queue c % kQueues; workgroup w starts on
+  // sub-queue w % kQueues (workgroups are spread over the XCDs round-robin, so each
+  // sub-queue has one XCD's workgroups as first takers).
   {
-    const int64_t nj = int64_t(jobs.size());
-    std::vector<int64_t> jc(nj);
-    int64_t total = 0, maxc = 0;
-    for (int64_t i = 0; i < nj; ++i) {
-      const JobRec& j = jobs[i];
-      const int64_t rows = std::min<int64_t>(j.rows, int64_t(j.tile_lo + j.tile_n) * 16) - int64_t(j.tile_lo) * 16;
-      jc[i] = std::max<int64_t>(rows, 128) * j.len;
-      total += jc[i];
-      maxc = std::max(maxc, jc[i]);
-    }
+    const int64_t total = jc_total, maxc = jc_max;
     int64_t h = nj, acc = 0;
     while (h > 0 && acc * 5 < total) acc += jc[--h];
     pl->tail_start = int32_t(h);
