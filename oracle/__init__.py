@@ -9,6 +9,8 @@ Contents
 --------
 attention  -- softmax attention by its definition, per-block partials (output +
               log-sum-exp), and the log-sum-exp merge.
+backward   -- the gradients dQ, dK, dV of softmax attention by their textbook
+              formulas, whole or one KV block at a time, and sampled entries.
 lpt        -- unit enumeration with the cost ``q_len x block_len x heads``, the
               longest-processing-time-first plan, its load-imbalance rate, and an
               exhaustive optimum for tiny instances.
@@ -25,6 +27,11 @@ attend_rows / attention_ref:
 partials_ref + merge_ref:
     split invariance (any partition of the keys, merged by log-sum-exp, equals the
     unsplit result), identity of an empty partial, invariance to block order.
+attention_grad_ref / grad_rows / grad_sample_ref:
+    central finite differences of the forward oracle (causal and not), the zero
+    upstream gradient, the closed form for identical value rows (dQ = dK = 0, the
+    dV rows summing to the summed upstream gradient), split invariance over block
+    sizes, and agreement of the sampled form with the whole one.
 lpt_ref / plan_ref:
     Graham's tight family (LPT = 4m-1 against OPT = 3m), Graham's 4/3 - 1/(3m)
     bound against ``opt_exhaustive`` on random tiny instances, the n <= m and
@@ -36,6 +43,7 @@ page to reproduce: parity unpinned (reported value only).
 """
 
 from .attention import attend_rows, attention_ref, partials_ref, merge_ref, sample_ref  # noqa: F401
+from .backward import attention_grad_ref, grad_rows, grad_sample_ref  # noqa: F401
 from .lpt import (  # noqa: F401
     enumerate_units,
     lpt_ref,
