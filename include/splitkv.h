@@ -52,7 +52,7 @@ extern "C" {
 #endif
 
 #define SPLITKV_VERSION_MAJOR 0
-#define SPLITKV_VERSION_MINOR 3
+#define SPLITKV_VERSION_MINOR 4
 
 typedef enum {
   SPLITKV_OK = 0,
@@ -215,6 +215,34 @@ int splitkv_merge(const splitkv_plan_t *plan, const void *dev_plan, const float 
  * as the two calls above. */
 int splitkv_attn(const splitkv_plan_t *plan, void *dev_plan, const splitkv_inputs *in,
                  float *ws, size_t ws_bytes, float *out, float *lse, void *hip_stream);
+
+/* Inputs of the backward pass besides Q, K and V (device memory, caller-owned). */
+typedef struct {
+  const void *d_out;                     /* upstream gradient dO [sum q, Hq, D], the dtype of q */
+  int64_t do_stride_tok, do_stride_head; /* its strides in elements (multiples of 16 bytes)     */
+  const float *out;                      /* the forward's O [sum q, Hq, D], contiguous          */
+  const float *lse;                      /* the forward's LSE [sum q, Hq] (natural log)          */
+  float *dq;                             /* written: dQ [sum q, Hq, D], contiguous               */
+  float *dk;                             /* written: dK [sum n, Hkv, D], contiguous              */
+  float *dv;                             /* written: dV [sum n, Hkv, D], contiguous              */
+} splitkv_grads;
+
+/* Backward pass of split-KV attention: dQ, dK, dV of sum(dO * O) with respect to Q, K
+ * and V, taken at the forward's O and LSE (from splitkv_attn on the same plan and
+ * inputs). Split-KV page, "Timeline": the sharded computation is exact; with the
+ * merged LSE every KV block's share of the gradients is exact on its own: a block's
+ * keys get their dK and dV from that block alone, and each query row's dQ is the sum
+ * of one query-sized part per block, summed here in block order (the same exchange
+ * as the forward's merge, with a plain sum). Textbook gradients:
+ *   D_i = <dO_i, O_i>, P = e^(scale q.k - LSE), dS = P (dO.v - D),
+ *   dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO,
+ * with dK and dV summed over the query heads of each KV head. bf16 inputs only;
+ * gradients fp32. The workspace (splitkv_plan_info.workspace_bytes) holds the dQ parts
+ * and D. The fields schedule and worker_clock of in are not used.
+ * Errors: INVALID_ARG (NULL or misaligned pointers, bad strides), UNSUPPORTED (fp32
+ * inputs, head_dim other than 64 or 128, bf16 strides beyond 2^24), WORKSPACE, HIP. */
+int splitkv_attn_backward(const splitkv_plan_t *plan, const void *dev_plan, const splitkv_inputs *in,
+                          const splitkv_grads *grads, float *ws, size_t ws_bytes, void *hip_stream);
 
 /* Static text for a status code. */
 const char *splitkv_status_string(int status);

@@ -2,7 +2,8 @@
 
 The computation lives in ``libsplitkv.so`` (C ABI, ``include/splitkv.h``): an LPT
 planner on the host and HIP kernels for per-block partial attention, the
-log-sum-exp merge, and the fused call. This package is its ctypes binding.
+log-sum-exp merge, the fused call, and the backward pass. This package is its ctypes
+binding.
 """
 
 from .api import (  # noqa: F401
@@ -10,6 +11,7 @@ from .api import (  # noqa: F401
     SplitKVError,
     plan_for,
     splitkv_attn,
+    splitkv_attn_backward,
     splitkv_merge,
     splitkv_partial_attn,
     splitkv_plan,

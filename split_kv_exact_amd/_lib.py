@@ -40,6 +40,7 @@ EXPORTED = (
     "splitkv_partial_attn",
     "splitkv_merge",
     "splitkv_attn",
+    "splitkv_attn_backward",
     "splitkv_status_string",
     "splitkv_last_error",
 )
@@ -95,6 +96,19 @@ class Inputs(ctypes.Structure):
     ]
 
 
+class Grads(ctypes.Structure):
+    _fields_ = [
+        ("d_out", ctypes.c_void_p),
+        ("do_stride_tok", ctypes.c_int64),
+        ("do_stride_head", ctypes.c_int64),
+        ("out", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p),
+        ("dk", ctypes.c_void_p),
+        ("dv", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -121,6 +135,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "splitkv_partial_attn": (ctypes.c_int, [P, P, ctypes.POINTER(Inputs), P, ctypes.c_size_t, P]),
         "splitkv_merge": (ctypes.c_int, [P, P, P, ctypes.c_size_t, P, P, P]),
         "splitkv_attn": (ctypes.c_int, [P, P, ctypes.POINTER(Inputs), P, ctypes.c_size_t, P, P, P]),
+        "splitkv_attn_backward": (ctypes.c_int, [P, P, ctypes.POINTER(Inputs), ctypes.POINTER(Grads), P,
+                                                 ctypes.c_size_t, P]),
         "splitkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "splitkv_last_error": (ctypes.c_char_p, []),
     }

@@ -256,6 +256,39 @@ def splitkv_attn(plan: Plan, dev_plan, q, k, v, ws=None, out=None, lse=None, sca
     return out, lse
 
 
+def splitkv_attn_backward(plan: Plan, dev_plan, q, k, v, do, out, lse, ws=None, dq=None, dk=None, dv=None,
+                          scale: float = 0.0, stream=None):
+    """Gradients dQ, dK, dV (fp32) of sum(do * out) at the forward's ``out`` and ``lse``
+    (``splitkv_attn_backward``; bf16 inputs)."""
+    torch = _torch()
+    _check_shapes(plan, q, k, v)
+    if do.shape != q.shape or do.dtype != q.dtype or do.stride(2) != 1:
+        raise ValueError("do must match q in shape and dtype, with contiguous head_dim")
+    for name, t in (("out", out), ("lse", lse)):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor")
+    if ws is None:
+        ws = workspace(plan, q.device)
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor shaped like {name[1]}")
+    inp = _inputs(q, k, v, scale)
+    gr = L.Grads(d_out=do.data_ptr(), do_stride_tok=do.stride(0), do_stride_head=do.stride(1), out=out.data_ptr(),
+                 lse=lse.data_ptr(), dq=dq.data_ptr(), dk=dk.data_ptr(), dv=dv.data_ptr())
+    _check(plan._lib, plan._lib.splitkv_attn_backward(plan.handle, ctypes.c_void_p(dev_plan.data_ptr()),
+                                                      ctypes.byref(inp), ctypes.byref(gr),
+                                                      ctypes.c_void_p(ws.data_ptr()),
+                                                      ws.numel() * ws.element_size(), _stream(stream)),
+           "splitkv_attn_backward")
+    return dq, dk, dv
+
+
 def status_string(status: int) -> str:
     return L.load().splitkv_status_string(status).decode()
 

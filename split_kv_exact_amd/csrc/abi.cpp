@@ -268,6 +268,67 @@ int splitkv_attn(const splitkv_plan_t* pl, void* dev_plan, const splitkv_inputs*
   return hip_status(splitkv::launch_merge(m, pl->D, stream), "merge launch");
 }
 
+int splitkv_attn_backward(const splitkv_plan_t* pl, const void* dev_plan, const splitkv_inputs* in,
+                          const splitkv_grads* gr, float* ws, size_t ws_bytes, void* hip_stream) {
+  g_last_error.clear();
+  if (int st = check_plan(pl, dev_plan)) return st;
+  float scale = 0.f;
+  if (int st = check_inputs(pl, in, &scale)) return st;
+  if (in->dtype != SPLITKV_BF16) return fail(SPLITKV_ERR_UNSUPPORTED, "the backward pass takes bf16 inputs only");
+  if (!gr) return fail(SPLITKV_ERR_INVALID_ARG, "grads is NULL");
+  if (!gr->d_out || !gr->out || !gr->lse || !gr->dq || !gr->dk || !gr->dv)
+    return fail(SPLITKV_ERR_INVALID_ARG, "d_out, out, lse, dq, dk and dv must be non-NULL");
+  if (!aligned16(gr->d_out) || !aligned16(gr->out) || !aligned16(gr->dq) || !aligned16(gr->dk) ||
+      !aligned16(gr->dv))
+    return fail(SPLITKV_ERR_INVALID_ARG, "d_out, out, dq, dk and dv must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(gr->lse) & 3u) != 0) return fail(SPLITKV_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  for (int64_t x : {gr->do_stride_tok, gr->do_stride_head}) {
+    if (x < 0 || x % 8 != 0) return fail(SPLITKV_ERR_INVALID_ARG, "d_out strides must be non-negative multiples of 16 bytes");
+    if (x > (int64_t(1) << 24)) return fail(SPLITKV_ERR_UNSUPPORTED, "bf16 strides must be at most 2^24 elements");
+  }
+  if (int st = check_ws(pl, ws, ws_bytes)) return st;
+  const uint8_t* base = static_cast<const uint8_t*>(dev_plan);
+  splitkv::BwdArgs b{};
+  b.q = in->q;
+  b.k = in->k;
+  b.v = in->v;
+  b.dout = gr->d_out;
+  b.q_st = in->q_stride_tok;
+  b.q_sh = in->q_stride_head;
+  b.k_st = in->k_stride_tok;
+  b.k_sh = in->k_stride_head;
+  b.v_st = in->v_stride_tok;
+  b.v_sh = in->v_stride_head;
+  b.do_st = gr->do_stride_tok;
+  b.do_sh = gr->do_stride_head;
+  b.scale = scale;
+  b.out = gr->out;
+  b.lse = gr->lse;
+  b.dq = gr->dq;
+  b.dk = gr->dk;
+  b.dv = gr->dv;
+  b.ws_dq = ws;
+  b.ws_d = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + pl->ws_lse_offset);
+  b.seqs = reinterpret_cast<const splitkv::SeqRec*>(base + pl->layout.seqs);
+  b.S = pl->S;
+  b.jobs = reinterpret_cast<const splitkv::JobRec*>(base + pl->layout.jobs);
+  b.num_jobs = int32_t(pl->num_jobs);
+  b.Hq = pl->Hq;
+  b.Hkv = pl->Hkv;
+  b.g = pl->g;
+  b.causal = pl->causal;
+  b.total_q = pl->total_q;
+  b.seq_ids = reinterpret_cast<const int32_t*>(base + pl->layout.merge_multi);
+  b.row_base = reinterpret_cast<const int64_t*>(base + pl->layout.merge_multi_base);
+  b.count = pl->num_multi;
+  b.total_rows = pl->merge_rows_multi;
+  int64_t tiles = 0;
+  for (const splitkv::SeqRec& r : pl->seqs) tiles += (r.n + 63) / 64;
+  b.key_tiles = tiles;
+  return hip_status(splitkv::launch_backward_bf16(b, pl->D, static_cast<hipStream_t>(hip_stream)),
+                    "backward launch");
+}
+
 const char* splitkv_status_string(int status) {
   switch (status) {
     case SPLITKV_OK: return "ok";

@@ -1,0 +1,519 @@
+// Gradients of split-KV attention on gfx950 matrix cores (bf16 inputs, fp32 math).
+//
+// Split-KV page, "Timeline": the sharded computation equals the unsharded one. With
+// the merged log-sum-exp of every query row, P = e^(S - LSE) is the row's global
+// softmax, so each context KV block's share of the backward pass is exact on its own
+// (textbook attention gradients, D_i = <dO_i, O_i>):
+//   dS = P o (dP - D),  dP = dO V^T,
+//   dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i   (complete within the block),
+//   dQ_i = scale sum_j dS_ij k_j                              (a query-sized part per block,
+//                                                              summed over the blocks).
+// The page describes no kernel; this is a CDNA4 design in four launches:
+//   rowdot:  D_i = <dO_i, O_i> for every query row (one wavefront per row);
+//   dq:      one workgroup per forward job (a unit's KV head and up to 256 of its query
+//            rows): its block's keys stream through LDS in stages of 32; each wave keeps
+//            Q, dO and its dQ part of two 16-row tiles in registers. Scores are computed
+//            transposed as in the forward (S^T = K Q^T), dP^T = V dO^T the same way, and
+//            dQ^T += K^T dS^T with K^T read by transposing LDS loads. The part goes to the
+//            workspace row of (block, KV head), or straight to dQ for one-block sequences;
+//   dqsum:   dQ of a multi-block sequence is the sum of its blocks' parts in block order
+//            (one wavefront per row);
+//   dkv:     one workgroup of 4 waves per (sequence, KV head, 64-key tile); a wave holds
+//            its 16 keys' K and V rows in registers and dK^T, dV^T accumulators, and the
+//            query rows that see the tile stream through LDS 32 at a time: S = Q K^T,
+//            dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS with Q^T and dO^T read by
+//            transposing loads. dK and dV are written once.
+// P and dS enter the matrix cores rounded to bf16 (as P does in the forward); all sums
+// are fp32.
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+#include "lds_tiles.hpp"
+
+namespace splitkv {
+namespace {
+
+using namespace lds;
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float NEG_INF = -__builtin_huge_valf();
+
+template <int D>
+struct BCfg {
+  static constexpr int DC = D / 32;      // 32-dim slices of a contraction over dims
+  static constexpr int DT = D / 16;      // 16-dim output tiles
+  static constexpr int ROWB = 2 * D;     // bytes per bf16 row
+  static constexpr int CH = ROWB / 16;   // 16-byte chunks per row
+  static constexpr int TILEB = 64 * ROWB;  // 64 rows
+};
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// ---------------------------------------------------------------- D_i = <dO_i, O_i>
+template <int D>
+__global__ __launch_bounds__(256) void rowdot_kernel(BwdArgs a) {
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);  // i * Hq + h
+  if (row >= a.total_q * a.Hq) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t i = row / a.Hq, h = row - i * a.Hq;
+  const __bf16* dop = reinterpret_cast<const __bf16*>(a.dout) + i * a.do_st + h * a.do_sh;
+  const float* op = a.out + row * D;
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < D / 64; ++k) s += float(dop[lane + 64 * k]) * op[lane + 64 * k];
+  s = wave_sum(s);
+  if (lane == 0) a.ws_d[row] = s;
+}
+
+// ---------------------------------------------------------------- dQ parts per job
+constexpr int DQ_WAVES = 8;
+constexpr int RT = 2;  // row tiles per wave
+
+constexpr int DQ_KEYS = 32;  // keys per stage (one step of the contraction)
+
+template <int D>
+struct DqLds {
+  unsigned char k[2][DQ_KEYS * BCfg<D>::ROWB];  // two stage buffers; K rows stored for transposing reads
+  unsigned char v[2][DQ_KEYS * BCfg<D>::ROWB];  // V rows stored for row reads
+};
+
+template <int D>
+__global__ __launch_bounds__(512) void dq_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using C = BCfg<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[sizeof(DqLds<D>)];
+  DqLds<D>& L = *reinterpret_cast<DqLds<D>*>(smem);
+  const JobRec j = a.jobs[blockIdx.x];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int G = lane >> 4, li = lane & 15;
+  const float c = a.scale * LOG2E;
+
+  // This wave's row tiles: tile_lo + wave and tile_lo + wave + 8.
+  int nt = 0;
+  int rowq[RT];  // query row of this lane in each tile (rows past the last repeat it)
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int tile = wave + t * DQ_WAVES;
+    if (tile < j.tile_n) nt = t + 1;
+    rowq[t] = min((j.tile_lo + min(tile, j.tile_n - 1)) * 16 + li, j.rows - 1);
+  }
+  bf16x8 qop[RT][C::DC], dop[RT][C::DC];
+  float lsec[RT], dd[RT];
+  int lim[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int r = rowq[t];
+    const int i = r / a.g, hl = r - i * a.g;
+    const int64_t tok = j.q_tok + i, head = int64_t(j.kv) * a.g + hl;
+    const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + tok * a.q_st + head * a.q_sh + 8 * G;
+    const __bf16* gp = reinterpret_cast<const __bf16*>(a.dout) + tok * a.do_st + head * a.do_sh + 8 * G;
+#pragma unroll
+    for (int dc = 0; dc < C::DC; ++dc) {
+      qop[t][dc] = *reinterpret_cast<const bf16x8*>(qp + 32 * dc);
+      dop[t][dc] = *reinterpret_cast<const bf16x8*>(gp + 32 * dc);
+    }
+    lsec[t] = a.lse[tok * a.Hq + head] * LOG2E;
+    dd[t] = a.ws_d[tok * a.Hq + head];
+    lim[t] = min(j.lim0 + i, j.len - 1);  // last visible block key of this row
+  }
+  f32x4 acc[RT][C::DT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) acc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Stage loads: 16-byte chunks, K then V, chunk index cidx = threadIdx.x + 512 u.
+  constexpr int NCH = DQ_KEYS * C::CH;                    // chunks per tile
+  constexpr int PER = (NCH + 511) / 512;                  // per thread per tile
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k) + 2 * (j.kv_tok * a.k_st + int64_t(j.kv) * a.k_sh);
+  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v) + 2 * (j.kv_tok * a.v_st + int64_t(j.kv) * a.v_sh);
+  u32x4 rk[PER], rv[PER];
+  auto load_stage = [&](int st) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int cidx = threadIdx.x + 512 * u;
+      const int key = min(st * DQ_KEYS + cidx / C::CH, j.len - 1);  // past the block: its last key (masked)
+      const int ch = cidx % C::CH;
+      rk[u] = *reinterpret_cast<const u32x4*>(kbase + int64_t(key) * (2 * a.k_st) + 16 * ch);
+      rv[u] = *reinterpret_cast<const u32x4*>(vbase + int64_t(key) * (2 * a.v_st) + 16 * ch);
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int cidx = threadIdx.x + 512 * u;
+      if (cidx < NCH) {
+        const int row = cidx / C::CH, ch = cidx % C::CH;
+        *reinterpret_cast<u32x4*>(L.k[buf] + row * C::ROWB + 16 * swz_tr<C::CH>(row, ch)) = rk[u];
+        *reinterpret_cast<u32x4*>(L.v[buf] + row * C::ROWB + 16 * swz_row<C::CH>(row, ch)) = rv[u];
+      }
+    }
+  };
+  // Per-lane LDS offsets within a 16-row tile: row reads (lane: row li, dims 8G + 32 dc)
+  // and K^T reads (lane: dims of tile dt, keys 4G + li/4 and 16 more).
+  unsigned ok_row[C::DC], ov_row[C::DC], ok_tr[C::DT];
+#pragma unroll
+  for (int dc = 0; dc < C::DC; ++dc) {
+    ok_row[dc] = li * C::ROWB + 16 * swz_tr<C::CH>(li, 4 * dc + G);
+    ov_row[dc] = li * C::ROWB + 16 * swz_row<C::CH>(li, 4 * dc + G);
+  }
+  {
+    const int e = li >> 2, cc = li & 3, r = 4 * G + e;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) ok_tr[dt] = r * C::ROWB + 16 * swz_tr<C::CH>(r, 2 * dt + (cc >> 1)) + 8 * (cc & 1);
+  }
+
+  const int nst = j.nst * (kStageKeys / DQ_KEYS);  // the job's stages of visible keys, in 32-key steps
+  load_stage(0);
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    store_stage(buf);
+    __syncthreads();
+    if (st + 1 < nst) load_stage(st + 1);
+    const unsigned kb = lds_addr(L.k[buf]), vb = lds_addr(L.v[buf]);
+    {
+      const int key0 = st * DQ_KEYS;  // block key of the stage's first key
+      if (nt > 0) {
+        // Per 16-key tile: S^T and dP^T, then dS^T = P^T (dP^T - D) with
+        // P^T = 2^(s c - LSE log2 e); entry e of tile tt is block key key0 + 16 tt + 4 G + e.
+        float ds[RT][2][4];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          bf16x8 kop[C::DC], vop[C::DC];
+          const unsigned rowoff = unsigned(tt * 16) * C::ROWB;
+#pragma unroll
+          for (int dc = 0; dc < C::DC; ++dc) {
+            kop[dc] = *reinterpret_cast<lds_bf16x8>(uintptr_t(kb + rowoff + ok_row[dc]));
+            vop[dc] = *reinterpret_cast<lds_bf16x8>(uintptr_t(vb + rowoff + ov_row[dc]));
+          }
+#pragma unroll
+          for (int t = 0; t < RT; ++t) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+            if (t < nt) {
+#pragma unroll
+              for (int dc = 0; dc < C::DC; ++dc) {
+                x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[dc], qop[t][dc], x, 0, 0, 0);
+                y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dc], dop[t][dc], y, 0, 0, 0);
+              }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int key = key0 + 16 * tt + 4 * G + e;
+              const float pr = key <= lim[t] ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c, -lsec[t])) : 0.f;
+              ds[t][tt][e] = pr * (y[e] - dd[t]);
+            }
+          }
+        }
+        bf16x8 dsb[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+          dsb[t] = bf16x8{(__bf16)ds[t][0][0], (__bf16)ds[t][0][1], (__bf16)ds[t][0][2], (__bf16)ds[t][0][3],
+                          (__bf16)ds[t][1][0], (__bf16)ds[t][1][1], (__bf16)ds[t][1][2], (__bf16)ds[t][1][3]};
+        // dQ^T += K^T dS^T over the stage's 32 keys.
+        unsigned ka[C::DT];
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) ka[dt] = kb + ok_tr[dt];
+        i16x4 lo[C::DT], hi[C::DT];
+        tr_read<0, 16 * C::ROWB>(lo, hi, ka);
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+          const bf16x8 kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[dt], hi[dt], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+            if (t < nt) acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, dsb[t], acc[t][dt], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();  // every wave is done with this buffer before it is refilled
+  }
+  // Store the part (lane: row li of the tile, dims 16 dt + 4 G .. + 3).
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    if (t < nt) {
+      const int r = rowq[t];
+      float* dst;
+      if (j.flags & kJobSingle) {
+        const int i = r / a.g, hl = r - i * a.g;
+        dst = a.dq + ((j.q_tok + i) * a.Hq + int64_t(j.kv) * a.g + hl) * D;
+      } else {
+        dst = a.ws_dq + (j.ws_row + r) * D;
+      }
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt + 4 * G) = acc[t][dt] * a.scale;
+    }
+  }
+#endif
+}
+
+// ---------------------------------------------------------------- dQ = sum of the parts
+template <int D>
+__global__ __launch_bounds__(256) void dqsum_kernel(BwdArgs a) {
+  constexpr int DPL = D / 64;
+  const int64_t gw = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (gw >= a.total_rows) return;
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = a.count - 1;  // sequence with row_base[lo] <= gw < row_base[lo + 1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.row_base[mid] <= gw)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const SeqRec sq = a.seqs[a.seq_ids[lo]];
+  const int64_t rem = gw - a.row_base[lo];
+  const int kv = int(rem / sq.rows);
+  const int r = int(rem - int64_t(kv) * sq.rows);
+  const int64_t r0 = sq.row_base + int64_t(kv) * sq.nb * sq.rows + r;  // block b: r0 + b * rows
+  float s[DPL];
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) s[k] = 0.f;
+  for (int b = 0; b < sq.nb; ++b) {
+    const float* p = a.ws_dq + (r0 + int64_t(b) * sq.rows) * D;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) s[k] += p[lane + 64 * k];
+  }
+  const int i = r / a.g, hl = r - i * a.g;
+  float* dst = a.dq + ((sq.q_base + i) * a.Hq + int64_t(kv) * a.g + hl) * D;
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) dst[lane + 64 * k] = s[k];
+}
+
+// ---------------------------------------------------------------- dK, dV per key tile
+constexpr int KV_WAVES = 4;
+constexpr int RCH = 32;  // query rows per chunk
+
+template <int D>
+struct KvLds {
+  unsigned char q[2][RCH * BCfg<D>::ROWB];   // Q rows, stored for row and transposing reads
+  unsigned char g[2][RCH * BCfg<D>::ROWB];   // dO rows, likewise
+  float lsec[2][RCH];                         // LSE * log2(e) (+inf for rows past the last)
+  float dd[2][RCH];                           // D_i
+  int pos[2][RCH];                            // position of the row's query token
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void dkv_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using C = BCfg<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[sizeof(KvLds<D>)];
+  KvLds<D>& L = *reinterpret_cast<KvLds<D>*>(smem);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int G = lane >> 4, li = lane & 15;
+  const float c = a.scale * LOG2E;
+
+  // Workgroup -> (sequence s, KV head kv, 64-key tile t).
+  const int64_t wg = blockIdx.x;
+  const int kv = int(wg % a.Hkv);
+  int64_t tile = wg / a.Hkv;
+  int s = 0;
+  for (;; ++s) {
+    const int64_t nt_s = (a.seqs[s].n + 63) / 64;
+    if (tile < nt_s || s + 1 == a.S) break;
+    tile -= nt_s;
+  }
+  const SeqRec sq = a.seqs[s];
+  const int64_t n = sq.n, k0 = tile * 64;
+  const int rows = sq.rows;  // q * g
+  // This lane's key (the wave's 16 keys) and its K and V rows as B operands
+  // (lane: key li, dims 8 G + 32 dc).
+  const int64_t key = k0 + 16 * wave + li;
+  const int64_t keyc = min(key, n - 1);
+  bf16x8 kt[C::DC], vt[C::DC];
+  {
+    const __bf16* kp = reinterpret_cast<const __bf16*>(a.k) + (sq.kv_base + keyc) * a.k_st + int64_t(kv) * a.k_sh + 8 * G;
+    const __bf16* vp = reinterpret_cast<const __bf16*>(a.v) + (sq.kv_base + keyc) * a.v_st + int64_t(kv) * a.v_sh + 8 * G;
+#pragma unroll
+    for (int dc = 0; dc < C::DC; ++dc) {
+      kt[dc] = *reinterpret_cast<const bf16x8*>(kp + 32 * dc);
+      vt[dc] = *reinterpret_cast<const bf16x8*>(vp + 32 * dc);
+    }
+  }
+  f32x4 dk[C::DT], dv[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Rows that see some key of the tile: query tokens i >= k0 - (n - q) when causal.
+  const int q = sq.q;
+  const int64_t i0 = a.causal ? max<int64_t>(0, k0 - (n - q)) : 0;
+  const int r_begin = int(i0) * a.g;
+  const int nchunk = r_begin < rows ? (rows - r_begin + RCH - 1) / RCH : 0;
+
+  // Chunk loads: Q and dO rows as 16-byte chunks (row = cidx / CH), 256 threads.
+  constexpr int NCH = RCH * C::CH;
+  constexpr int PER = (NCH + 255) / 256;
+  u32x4 rq[PER], rg[PER];
+  float r_l = 0.f, r_d = 0.f;
+  int r_p = 0;
+  auto row_src = [&](int r, int64_t& tok, int64_t& head) {
+    const int i = r / a.g, hl = r - i * a.g;
+    tok = sq.q_base + i;
+    head = int64_t(kv) * a.g + hl;
+  };
+  auto load_chunk = [&](int ch) {
+    const int rb = r_begin + ch * RCH;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int cidx = threadIdx.x + 256 * u;
+      const int r = min(rb + cidx / C::CH, rows - 1);
+      const int cc = cidx % C::CH;
+      int64_t tok, head;
+      row_src(r, tok, head);
+      rq[u] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(a.q) + 2 * (tok * a.q_st + head * a.q_sh) + 16 * cc);
+      rg[u] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(a.dout) + 2 * (tok * a.do_st + head * a.do_sh) + 16 * cc);
+    }
+    if (threadIdx.x < RCH) {
+      const int r = rb + threadIdx.x;
+      int64_t tok, head;
+      row_src(min(r, rows - 1), tok, head);
+      r_l = r < rows ? a.lse[tok * a.Hq + head] * LOG2E : __builtin_huge_valf();
+      r_d = a.ws_d[tok * a.Hq + head];
+      r_p = int(n - q + (min(r, rows - 1) / a.g));
+    }
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int cidx = threadIdx.x + 256 * u;
+      if (cidx < NCH) {
+        const int row = cidx / C::CH, cc = cidx % C::CH;
+        const int off = row * C::ROWB + 16 * swz_tr<C::CH>(row, cc);
+        *reinterpret_cast<u32x4*>(L.q[buf] + off) = rq[u];
+        *reinterpret_cast<u32x4*>(L.g[buf] + off) = rg[u];
+      }
+    }
+    if (threadIdx.x < RCH) {
+      L.lsec[buf][threadIdx.x] = r_l;
+      L.dd[buf][threadIdx.x] = r_d;
+      L.pos[buf][threadIdx.x] = r_p;
+    }
+  };
+  // Lane offsets within a 16-row tile of a chunk: row reads (lane: row li, dims 8G + 32dc)
+  // and transposing reads (lane: dims of tile dt, rows 4G + li/4 and 16 more).
+  unsigned o_row[C::DC], o_tr[C::DT];
+#pragma unroll
+  for (int dc = 0; dc < C::DC; ++dc) o_row[dc] = li * C::ROWB + 16 * swz_tr<C::CH>(li, 4 * dc + G);
+  {
+    const int e = li >> 2, cc = li & 3, r = 4 * G + e;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) o_tr[dt] = r * C::ROWB + 16 * swz_tr<C::CH>(r, 2 * dt + (cc >> 1)) + 8 * (cc & 1);
+  }
+
+  if (nchunk > 0) load_chunk(0);
+  for (int ch = 0; ch < nchunk; ++ch) {
+    const int buf = ch & 1;
+    store_chunk(buf);
+    __syncthreads();
+    if (ch + 1 < nchunk) load_chunk(ch + 1);
+    const unsigned qb = lds_addr(L.q[buf]), gb = lds_addr(L.g[buf]);
+    // S and dP for the chunk's two 16-row tiles (lane: key li, rows 16 t + 4 G + e).
+    f32x4 sv[2], pv[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf16x8 qa[C::DC], ga[C::DC];
+#pragma unroll
+      for (int dc = 0; dc < C::DC; ++dc) {
+        qa[dc] = *reinterpret_cast<lds_bf16x8>(uintptr_t(qb + unsigned(16 * t) * C::ROWB + o_row[dc]));
+        ga[dc] = *reinterpret_cast<lds_bf16x8>(uintptr_t(gb + unsigned(16 * t) * C::ROWB + o_row[dc]));
+      }
+      f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dc = 0; dc < C::DC; ++dc) {
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[dc], kt[dc], x, 0, 0, 0);
+        y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[dc], vt[dc], y, 0, 0, 0);
+      }
+      sv[t] = x;
+      pv[t] = y;
+    }
+    // P and dS (rows past the last have LSE = +inf, so P = 0).
+    float pr[2][4], ds[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = 16 * t + 4 * G + e;
+        const bool vis = key < n && (!a.causal || key <= L.pos[buf][rr]);
+        pr[t][e] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t][e], c, -L.lsec[buf][rr])) : 0.f;
+        ds[t][e] = pr[t][e] * (pv[t][e] - L.dd[buf][rr]);
+      }
+    const bf16x8 pb = {(__bf16)pr[0][0], (__bf16)pr[0][1], (__bf16)pr[0][2], (__bf16)pr[0][3],
+                       (__bf16)pr[1][0], (__bf16)pr[1][1], (__bf16)pr[1][2], (__bf16)pr[1][3]};
+    const bf16x8 db = {(__bf16)ds[0][0], (__bf16)ds[0][1], (__bf16)ds[0][2], (__bf16)ds[0][3],
+                       (__bf16)ds[1][0], (__bf16)ds[1][1], (__bf16)ds[1][2], (__bf16)ds[1][3]};
+    // dV^T += dO^T P and dK^T += Q^T dS over the chunk's 32 rows.
+    {
+      unsigned ga[C::DT];
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) ga[dt] = gb + o_tr[dt];
+      i16x4 lo[C::DT], hi[C::DT];
+      tr_read<0, 16 * C::ROWB>(lo, hi, ga);
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+        dv[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[dt], hi[dt], 0, 1, 2, 3, 4, 5, 6, 7)), pb, dv[dt], 0, 0, 0);
+    }
+    {
+      unsigned qa[C::DT];
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) qa[dt] = qb + o_tr[dt];
+      i16x4 lo[C::DT], hi[C::DT];
+      tr_read<0, 16 * C::ROWB>(lo, hi, qa);
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+        dk[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[dt], hi[dt], 0, 1, 2, 3, 4, 5, 6, 7)), db, dk[dt], 0, 0, 0);
+    }
+    __syncthreads();  // every wave is done with this buffer before it is refilled
+  }
+  // Store (lane: key li, dims 16 dt + 4 G .. + 3); keys past the sequence are not stored.
+  if (key < n) {
+    const int64_t idx = ((sq.kv_base + key) * a.Hkv + kv) * D;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      *reinterpret_cast<f32x4*>(a.dk + idx + 16 * dt + 4 * G) = dk[dt] * a.scale;
+      *reinterpret_cast<f32x4*>(a.dv + idx + 16 * dt + 4 * G) = dv[dt];
+    }
+  }
+#endif
+}
+
+template <int D>
+hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
+  const int64_t qrows = a.total_q * a.Hq;
+  if (qrows > 0) {
+    hipLaunchKernelGGL(rowdot_kernel<D>, dim3(unsigned((qrows + 3) / 4)), dim3(256), 0, stream, a);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  if (a.num_jobs > 0) {
+    hipLaunchKernelGGL(dq_kernel<D>, dim3(unsigned(a.num_jobs)), dim3(512), 0, stream, a);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  if (a.total_rows > 0) {
+    hipLaunchKernelGGL(dqsum_kernel<D>, dim3(unsigned((a.total_rows + 3) / 4)), dim3(256), 0, stream, a);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  if (a.key_tiles > 0) {
+    hipLaunchKernelGGL(dkv_kernel<D>, dim3(unsigned(a.key_tiles * a.Hkv)), dim3(256), 0, stream, a);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_backward_bf16(const BwdArgs& a, int head_dim, hipStream_t stream) {
+  if ((a.total_q * a.Hq + 3) / 4 > 0x7fffffffLL || a.num_jobs > 0x7fffffff || (a.total_rows + 3) / 4 > 0x7fffffffLL ||
+      a.key_tiles * a.Hkv > 0x7fffffffLL)
+    return hipErrorInvalidValue;
+  if (head_dim == 128) return launch_all<128>(a, stream);
+  if (head_dim == 64) return launch_all<64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace splitkv

@@ -52,7 +52,37 @@ struct MergeArgs {
   float* lse;
 };
 
+// Arguments of the backward kernels (bf16 inputs, fp32 gradients).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;                                    // dO, same dtype as q
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, do_st, do_sh;  // strides in elements
+  float scale;
+  const float* out;  // forward O [total_q, Hq, D], contiguous
+  const float* lse;  // forward LSE [total_q, Hq]
+  float* dq;         // [total_q, Hq, D], contiguous
+  float* dk;         // [total_kv, Hkv, D], contiguous
+  float* dv;
+  float* ws_dq;      // per (block, KV head) dQ parts [partial_rows, D]
+  float* ws_d;       // D_i = <dO_i, O_i> [total_q * Hq]
+  const SeqRec* seqs;
+  int32_t S;
+  const JobRec* jobs;
+  int32_t num_jobs;
+  int32_t Hq, Hkv, g, causal;
+  int64_t total_q;
+  // Summing the dQ parts of multi-block sequences (the merge's row mapping).
+  const int32_t* seq_ids;
+  const int64_t* row_base;
+  int32_t count;
+  int64_t total_rows;
+  int64_t key_tiles;  // sum over sequences of ceil(n_s / 64)
+};
+
 hipError_t launch_partial_bf16(const PartialArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_backward_bf16(const BwdArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_partial_f32(const PartialArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
 

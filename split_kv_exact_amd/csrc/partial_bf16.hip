@@ -46,17 +46,12 @@
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
+#include "lds_tiles.hpp"
 
 namespace splitkv {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) const bf16x8* lds_bf16x8;
+using namespace lds;
 
 constexpr int NW = 8;           // wavefronts per workgroup (two per SIMD)
 constexpr int TK = kStageKeys;  // keys per pipeline stage
@@ -93,9 +88,9 @@ struct Cfg {
 // reads (K, Q) and 32-lane transposing reads (V). Both depend on the row modulo 16
 // only, and tiles start at multiples of 16 rows.
 template <int D>
-__device__ __forceinline__ int swz_k(int row, int c) { return c ^ (row & (Cfg<D>::CH - 1)); }
+__device__ __forceinline__ int swz_k(int row, int c) { return swz_row<Cfg<D>::CH>(row, c); }
 template <int D>
-__device__ __forceinline__ int swz_v(int row, int c) { return c ^ ((2 * row) & (Cfg<D>::CH - 1)); }
+__device__ __forceinline__ int swz_v(int row, int c) { return swz_tr<Cfg<D>::CH>(row, c); }
 
 // Wait until at most n vector-memory instructions of this wave are outstanding, then
 // barrier the workgroup (no fence: the pipeline's later DMA must stay in flight).
@@ -131,47 +126,6 @@ __device__ __forceinline__ void wait_stage(int n) {
 // LDS writes and reads of this wave done, then barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__device__ __forceinline__ unsigned lds_addr(const unsigned char* p) {
-  typedef __attribute__((address_space(3))) const unsigned char* lds_cptr;
-  return (unsigned)(uintptr_t)(lds_cptr)p;  // 32-bit LDS offset
-}
-
-// Transposing LDS reads (ds_read_b64_tr_b16) issued from inline assembly. Through the
-// builtin, the compiler cannot tell that they read a different pipeline slot than the
-// in-flight DMA writes, and it drains all of that DMA first. The reads and their
-// lgkmcnt wait sit in one asm statement, so no instruction can touch the destination
-// registers while the loads are still in flight. Lane addresses are a[dt] + OFF (keys
-// 0-15 of the step) and a[dt] + OFF + HI (keys 16-31).
-template <int OFF, int HI>
-__device__ __forceinline__ void tr_read(i16x4 (&lo)[8], i16x4 (&hi)[8], const unsigned (&a)[8]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %16 offset:%24\n\tds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %2, %18 offset:%24\n\tds_read_b64_tr_b16 %3, %19 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %4, %20 offset:%24\n\tds_read_b64_tr_b16 %5, %21 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %6, %22 offset:%24\n\tds_read_b64_tr_b16 %7, %23 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %8, %16 offset:%25\n\tds_read_b64_tr_b16 %9, %17 offset:%25\n\t"
-      "ds_read_b64_tr_b16 %10, %18 offset:%25\n\tds_read_b64_tr_b16 %11, %19 offset:%25\n\t"
-      "ds_read_b64_tr_b16 %12, %20 offset:%25\n\tds_read_b64_tr_b16 %13, %21 offset:%25\n\t"
-      "ds_read_b64_tr_b16 %14, %22 offset:%25\n\tds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(lo[4]), "=&v"(lo[5]), "=&v"(lo[6]),
-        "=&v"(lo[7]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]), "=&v"(hi[3]), "=&v"(hi[4]), "=&v"(hi[5]),
-        "=&v"(hi[6]), "=&v"(hi[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF),
-        "i"(OFF + HI));
-}
-template <int OFF, int HI>
-__device__ __forceinline__ void tr_read(i16x4 (&lo)[4], i16x4 (&hi)[4], const unsigned (&a)[4]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\tds_read_b64_tr_b16 %1, %9 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %2, %10 offset:%12\n\tds_read_b64_tr_b16 %3, %11 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %4, %8 offset:%13\n\tds_read_b64_tr_b16 %5, %9 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %6, %10 offset:%13\n\tds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]),
-        "=&v"(hi[3])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF), "i"(OFF + HI));
-}
 
 __device__ __forceinline__ float max4(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));

@@ -161,6 +161,33 @@ def test_merge_and_attn_argument_errors(lib):
     lib.splitkv_plan_destroy(h)
 
 
+def test_backward_argument_errors(lib):
+    h, inf = _plan_handle(lib)
+    dp, ws, nbytes = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), inf.workspace_bytes
+    f = lib.splitkv_attn_backward
+
+    def grads(**kw):
+        g = dict(d_out=FAKE, do_stride_tok=256, do_stride_head=128, out=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE)
+        g.update(kw)
+        return L.Grads(**g)
+
+    good = _inputs()
+    assert f(h, dp, ctypes.byref(good), None, ws, nbytes, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, dp, ctypes.byref(_inputs(dtype=L.SPLITKV_F32)), ctypes.byref(grads()), ws, nbytes,
+             None) == L.SPLITKV_ERR_UNSUPPORTED
+    assert f(h, dp, ctypes.byref(good), ctypes.byref(grads(d_out=0)), ws, nbytes, None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, dp, ctypes.byref(good), ctypes.byref(grads(dk=FAKE + 4)), ws, nbytes,
+             None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, dp, ctypes.byref(good), ctypes.byref(grads(lse=FAKE + 2)), ws, nbytes,
+             None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, dp, ctypes.byref(good), ctypes.byref(grads(do_stride_head=100)), ws, nbytes,
+             None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, dp, ctypes.byref(good), ctypes.byref(grads(do_stride_tok=1 << 25)), ws, nbytes,
+             None) == L.SPLITKV_ERR_UNSUPPORTED
+    assert f(h, dp, ctypes.byref(good), ctypes.byref(grads()), ws, 16, None) == L.SPLITKV_ERR_WORKSPACE
+    lib.splitkv_plan_destroy(h)
+
+
 def test_plan_info_sizes():
     pl = splitkv_plan([100, 40], [3, 1], 4, 2, 128, 64, 8)
     inf = pl.info()

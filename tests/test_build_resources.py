@@ -46,7 +46,7 @@ def _resources(src):
     return kernels
 
 
-@pytest.mark.parametrize("src", ["partial_bf16.hip", "partial_f32.hip", "merge.hip"])
+@pytest.mark.parametrize("src", ["partial_bf16.hip", "partial_f32.hip", "merge.hip", "backward_bf16.hip"])
 def test_no_scratch_and_no_spills(src):
     ks = _resources(src)
     assert ks, "no kernels reported"

@@ -1,0 +1,132 @@
+"""GPU parity of the backward pass: libsplitkv's gradients against the float64 oracle.
+
+The oracle evaluates the textbook gradients at the forward outputs the GPU produced
+(O and LSE from splitkv_attn), so the comparison isolates the backward kernels. Small
+cases run the whole oracle; a full-size workload is checked on sampled gradient rows.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import split_kv_exact_amd as skv
+from oracle.backward import attention_grad_ref, grad_sample_ref
+from tests.parity import say
+from workloads import Workload, get_workload, make_qkv, widen_to_f64
+
+pytestmark = pytest.mark.gpu
+
+# Tolerances (bf16 inputs; P and dS are rounded to bf16 before the matrix products, as
+# P is in the forward): relative L2 error of each gradient tensor, and the largest
+# element error relative to the tensor's largest magnitude. See the design notes for
+# the derivation.
+REL_L2 = 1e-2
+REL_MAX = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _wl(name, kv, q, hq, hkv, d, b, m, causal=True, gran=0, seed=21, boost_frac=0.0):
+    return Workload(name=name, dtype="bfloat16", kv_lens=tuple(kv), q_lens=tuple(q), num_q_heads=hq,
+                    num_kv_heads=hkv, head_dim=d, block_len=b, num_workers=m, causal=causal, seed=seed,
+                    boost_frac=boost_frac, boost=8.0, granularity=gran)
+
+
+CASES = [
+    _wl("ragged_d128", [1000, 333, 77, 2100, 16], [16, 5, 1, 40, 16], 32, 8, 128, 256, 16),
+    _wl("ragged_d64", [1000, 333, 77, 513], [16, 5, 1, 9], 8, 2, 64, 128, 7),
+    _wl("noncausal", [700, 45], [12, 3], 16, 4, 128, 128, 9, causal=False),
+    _wl("whole_block_units", [900, 260], [8, 2], 16, 4, 128, 256, 6, gran=1),
+    _wl("q_equals_n", [1, 5, 64, 2, 3], [1, 5, 64, 1, 3], 8, 4, 128, 16, 11),
+    _wl("single_block", [100, 37], [3, 2], 8, 2, 128, 4096, 4),
+    _wl("two_row_passes", [2048], [300], 32, 8, 128, 512, 8),
+    _wl("boosted_keys", [3000, 1500], [16, 1], 64, 8, 128, 512, 32, boost_frac=0.01),
+]
+
+
+def _do(wl, seed=99):
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    return torch.randn((wl.total_q, wl.num_q_heads, wl.head_dim), generator=gen, device="cuda",
+                       dtype=torch.float32).to(torch.bfloat16)
+
+
+def _errors(got, ref):
+    d = got - ref
+    scale = max(np.abs(ref).max(), 1e-30)
+    return float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-30)), float(np.abs(d).max() / scale)
+
+
+def _forward_backward(wl):
+    q, k, v = make_qkv(wl, "cuda")
+    do = _do(wl)
+    plan = skv.plan_for(wl)
+    dev_plan = skv.splitkv_plan_upload(plan)
+    out, lse = skv.splitkv_attn(plan, dev_plan, q, k, v)
+    ws = skv.workspace(plan)
+    ws.fill_(float("nan"))
+    dq = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    dk = torch.full(k.shape, float("nan"), dtype=torch.float32, device="cuda")
+    dv = torch.full(v.shape, float("nan"), dtype=torch.float32, device="cuda")
+    skv.splitkv_attn_backward(plan, dev_plan, q, k, v, do, out, lse, ws, dq, dk, dv)
+    torch.cuda.synchronize()
+    return q, k, v, do, out, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("wl", CASES, ids=[w.name for w in CASES])
+def test_small_backward_against_oracle(wl):
+    say(f"[gpu] backward {wl.name}")
+    q, k, v, do, out, lse, dq, dk, dv = _forward_backward(wl)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert not torch.isnan(t).any(), f"{name} has unwritten entries"
+    ref = attention_grad_ref(widen_to_f64(q), widen_to_f64(k), widen_to_f64(v), widen_to_f64(do), wl.kv_lens,
+                             wl.q_lens, wl.num_q_heads, wl.num_kv_heads, wl.causal,
+                             o=widen_to_f64(out), lse=widen_to_f64(lse))
+    for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        l2, mx = _errors(widen_to_f64(got), r)
+        say(f"    {name}: rel L2 {l2:.2e}, max |d| / max |ref| {mx:.2e}")
+        assert l2 <= REL_L2 and mx <= REL_MAX, (name, l2, mx)
+
+
+def test_backward_is_deterministic():
+    wl = CASES[0]
+    a = _forward_backward(wl)
+    b = _forward_backward(wl)
+    for x, y in zip(a[6:], b[6:]):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("key", ["batch8"])
+def test_full_size_backward_sampled(key):
+    """Full-size workload in the benchmark's launch configuration, checked on sampled
+    dQ rows and dK / dV keys of two sequences against the oracle at the GPU's forward
+    outputs."""
+    wl = get_workload(key)
+    say(f"[gpu] full-size backward {wl.name}")
+    q, k, v, do, out, lse, dq, dk, dv = _forward_backward(wl)
+    rng = np.random.default_rng(5)
+    qo = np.concatenate([[0], np.cumsum(wl.q_lens)])
+    ko = np.concatenate([[0], np.cumsum(wl.kv_lens)])
+    for s in (0, wl.batch - 1):
+        n, qs = wl.kv_lens[s], wl.q_lens[s]
+        pairs = sorted({(int(rng.integers(0, qs)), int(rng.integers(0, wl.num_q_heads))) for _ in range(6)})
+        keys = sorted({(int(rng.integers(0, n)), int(rng.integers(0, wl.num_kv_heads))) for _ in range(6)}
+                      | {(n - 1, 0), (0, wl.num_kv_heads - 1)})
+        sl, kl = slice(qo[s], qo[s + 1]), slice(ko[s], ko[s + 1])
+        rq, rk, rv = grad_sample_ref(widen_to_f64(q[sl]), widen_to_f64(k[kl]), widen_to_f64(v[kl]),
+                                     widen_to_f64(do[sl]), widen_to_f64(out[sl]), widen_to_f64(lse[sl]),
+                                     wl.num_kv_heads, pairs, keys, wl.causal)
+        gq = np.stack([widen_to_f64(dq[qo[s] + i, h]) for i, h in pairs])
+        gk = np.stack([widen_to_f64(dk[ko[s] + j, c]) for j, c in keys])
+        gv = np.stack([widen_to_f64(dv[ko[s] + j, c]) for j, c in keys])
+        for name, got, r in (("dq", gq, rq), ("dk", gk, rk), ("dv", gv, rv)):
+            l2, mx = _errors(got, r)
+            say(f"    seq {s} {name}: rel L2 {l2:.2e}, max |d| / max |ref| {mx:.2e}")
+            assert l2 <= REL_L2 and mx <= REL_MAX, (s, name, l2, mx)
