@@ -157,6 +157,8 @@ def main() -> int:
     ap.add_argument("--cost-ridge", type=int, default=0,
                     help="LPT unit cost: 0 = q * len * heads (the pages' cost); R > 0 = len * max(q * g, R) "
                          "per KV head (roofline-aware, R = ridge in query rows)")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the backward pass (splitkv_attn_backward) and report it under 'backward'")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (a kernel of known traffic, for scaling "
                          "hardware byte counters)")
@@ -325,11 +327,49 @@ def main() -> int:
         "workspace_bytes": info["workspace_bytes"],
         "kernel_sha": _kernel_sha(),
     }
+    if args.backward:
+        result["backward"] = (_bench_backward(skv, M, wl, plan, dev_plan, q, k, v, ws, out, lse, stream, args)
+                              if wl.dtype == "bfloat16" else None)  # the backward takes bf16 inputs
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_budget)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def _bench_backward(skv, M, wl, plan, dev_plan, q, k, v, ws, out, lse, stream, args):
+    """Times splitkv_attn_backward (its four launches together) at the forward's O and
+    LSE, with a seeded upstream gradient."""
+    import torch
+
+    print("[bench] backward", file=sys.stderr, flush=True)
+    gen = torch.Generator(device=q.device)
+    gen.manual_seed(99)
+    do = torch.randn(q.shape, generator=gen, device=q.device, dtype=torch.float32).to(q.dtype)
+    skv.splitkv_attn(plan, dev_plan, q, k, v, ws, out, lse)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+
+    def bstep():
+        skv.splitkv_attn_backward(plan, dev_plan, q, k, v, do, out, lse, ws, dq, dk, dv)
+
+    for _ in range(max(1, args.warmup)):
+        bstep()
+    ms = _time_loop(bstep, max(3, min(args.steps, 10)), stream)
+    fl, by = M.backward_flops(wl), M.backward_bytes(wl)
+    tr = M.backward_roofline_seconds(wl)
+    bound = "mfma" if fl / (M.PEAK_BF16_MFMA_TFLOPS * 1e12) >= by / (M.PEAK_HBM_GBS * 1e9) else "hbm"
+    return {
+        "ms_per_call": round(ms, 5),
+        "tflops": round(fl / (ms * 1e-3) / 1e12, 3),
+        "gbs": round(by / (ms * 1e-3) / 1e9, 2),
+        "flops": fl,
+        "bytes": by,
+        "bound": bound,
+        "roofline_fraction": round(tr / (ms * 1e-3), 4),
+        "note": "flops 10*D per visible (row, key) pair; bytes Q, K, V, dO, O, LSE read once, dQ, dK, dV written",
+    }
 
 
 if __name__ == "__main__":

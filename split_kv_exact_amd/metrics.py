@@ -66,3 +66,25 @@ def roofline_seconds(wl) -> float:
 def binding_roof(wl) -> str:
     peak_f = PEAK_FP32_VECTOR_TFLOPS if wl.dtype == "float32" else PEAK_BF16_MFMA_TFLOPS
     return "hbm" if effective_bytes(wl) / (PEAK_HBM_GBS * 1e9) >= flops(wl) / (peak_f * 1e12) else "mfma"
+
+
+def backward_flops(wl) -> int:
+    """Backward pass: five products per visible (row, key) pair and dimension pair of
+    multiply-adds (S = Q K^T recomputed, dP = dO V^T, dV = P^T dO, dK = dS^T Q,
+    dQ = dS K), 10 * D flops per pair: 2.5 times the forward."""
+    return 10 * wl.head_dim * wl.num_q_heads * visible_pairs(wl)
+
+
+def backward_bytes(wl) -> int:
+    """Backward pass, each element once: Q, K, V and dO read in the input dtype, O and
+    LSE read and dQ, dK, dV written in fp32."""
+    es = 2 if wl.dtype == "bfloat16" else 4
+    d = wl.head_dim
+    q_elems = wl.total_q * wl.num_q_heads * d
+    kv_elems = wl.total_kv * wl.num_kv_heads * d
+    return (2 * q_elems + 2 * kv_elems) * es + (q_elems + wl.total_q * wl.num_q_heads) * 4 \
+        + (q_elems + 2 * kv_elems) * 4
+
+
+def backward_roofline_seconds(wl) -> float:
+    return max(backward_bytes(wl) / (PEAK_HBM_GBS * 1e9), backward_flops(wl) / (PEAK_BF16_MFMA_TFLOPS * 1e12))
