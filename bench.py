@@ -159,11 +159,17 @@ def main() -> int:
                          "per KV head (roofline-aware, R = ridge in query rows)")
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward pass (splitkv_attn_backward) and report it under 'backward'")
+    ap.add_argument("--planner-study", action="store_true",
+                    help="host only: time the LPT planner against an exact MILP balancer (HiGHS) on small "
+                         "instances cut from the workloads, and on the full workloads, then exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (a kernel of known traffic, for scaling "
                          "hardware byte counters)")
     args = ap.parse_args()
 
+    if args.planner_study:
+        print(json.dumps(planner_study()), flush=True)
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: split-KV here runs on the 256 CUs of a single MI355X; "
               "multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
@@ -335,6 +341,83 @@ def main() -> int:
         result["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_budget)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def planner_study(milp_seconds: float = 20.0):
+    """The Split-KV page ("Timeline") reports LPT planning three orders of magnitude
+    faster than the best load-balancing baseline, which it does not name. Here the
+    baseline is the exact one: the makespan MILP (x[u, w] binary, min C subject to
+    every unit on one worker and every worker's load <= C), solved by HiGHS through
+    SciPy with a time limit. Instances are the first sequences of the lognormal and
+    mixed workloads with fewer heads and workers, so that the MILP stays small; the
+    C++ planner's time on the full workloads is reported beside them."""
+    import numpy as np
+    from scipy.optimize import Bounds, LinearConstraint, milp
+
+    import split_kv_exact_amd as skv
+    from workloads import get_workload
+
+    def c_plan(kv, ql, hq, hkv, b, m):
+        times = []
+        for _ in range(20):
+            t0 = time.perf_counter_ns()
+            pl = skv.splitkv_plan(kv, ql, hq, hkv, 128, b, m, True, 0)
+            times.append((time.perf_counter_ns() - t0) / 1e3)
+        times.sort()
+        return pl, times[len(times) // 2]
+
+    def exact(costs, m):
+        n = len(costs)
+        nv = n * m + 1
+        obj = np.zeros(nv)
+        obj[-1] = 1.0
+        a1 = np.zeros((n, nv))
+        a2 = np.zeros((m, nv))
+        for u in range(n):
+            a1[u, u * m:(u + 1) * m] = 1.0
+        for w in range(m):
+            a2[w, w:n * m:m] = costs
+            a2[w, -1] = -1.0
+        integ = np.ones(nv)
+        integ[-1] = 0
+        t0 = time.perf_counter()
+        r = milp(obj, constraints=[LinearConstraint(a1, 1, 1), LinearConstraint(a2, -np.inf, 0)], integrality=integ,
+                 bounds=Bounds(0, np.r_[np.ones(n * m), np.inf]), options={"time_limit": milp_seconds})
+        return r, time.perf_counter() - t0
+
+    rows = []
+    for key, nseq, hq, hkv, b, m in (("lognormal", 2, 4, 1, 4096, 4), ("lognormal", 4, 4, 1, 4096, 8),
+                                     ("mixed", 3, 8, 1, 4096, 8), ("mixed", 132, 8, 1, 65536, 16)):
+        wl = get_workload(key)
+        kv, ql = list(wl.kv_lens[:nseq]), list(wl.q_lens[:nseq])
+        if key == "mixed" and nseq == 3:
+            kv, ql = [kv[0], kv[1], wl.kv_lens[-1]], [ql[0], ql[1], wl.q_lens[-1]]  # two decode, one prefill
+        pl, us = c_plan(kv, ql, hq, hkv, b, m)
+        costs = pl.export()["unit_cost"].astype(np.float64)
+        inf = pl.info()
+        r, sec = exact(costs, m)
+        rows.append({
+            "instance": f"{key}: {len(kv)} sequences, Hq/Hkv {hq}/{hkv}, block {b}, {m} workers",
+            "units": int(inf["num_units"]),
+            "lpt_makespan": int(inf["makespan"]),
+            "lower_bound": int(inf["lower_bound"]),
+            "lpt_us": round(us, 1),
+            "milp_makespan": None if r.x is None else int(round(r.fun)),
+            "milp_proved_bound": None if getattr(r, "mip_dual_bound", None) is None else float(r.mip_dual_bound),
+            "milp_optimal": bool(r.status == 0),
+            "milp_s": round(sec, 2),
+        })
+    full = []
+    for key in ("lognormal", "mixed", "batch8"):
+        wl = get_workload(key)
+        pl, us = c_plan(wl.kv_lens, wl.q_lens, wl.num_q_heads, wl.num_kv_heads, wl.block_len, wl.num_workers)
+        inf = pl.info()
+        full.append({"workload": wl.name, "units": int(inf["num_units"]), "workers": wl.num_workers,
+                     "lpt_ms": round(us / 1e3, 3), "imbalance": inf["imbalance"],
+                     "makespan_over_lower_bound": inf["makespan"] / inf["lower_bound"],
+                     "milp_binaries": int(inf["num_units"]) * wl.num_workers})
+    return {"study": "LPT planner against an exact makespan MILP (HiGHS via SciPy, "
+                     f"{milp_seconds:.0f} s limit)", "instances": rows, "full_workloads": full}
 
 
 def _bench_backward(skv, M, wl, plan, dev_plan, q, k, v, ws, out, lse, stream, args):
