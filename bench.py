@@ -29,7 +29,7 @@ METRIC = "split-KV attention+merge effective HBM GB/s & TFLOP/s, % of MI355X roo
 def _kernel_sha() -> str:
     h = hashlib.sha256()
     for f in ("partial_bf16.hip", "partial_f32.hip", "merge.hip", "abi.cpp", "plan.cpp", "kernels.hpp",
-              "plan_image.hpp"):
+              "plan_image.hpp", "lds_tiles.hpp"):
         with open(os.path.join(ROOT, "split_kv_exact_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
