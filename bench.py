@@ -19,6 +19,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -94,7 +96,6 @@ def cpu_baseline(wl, q, k, v, budget_s: float):
     """Time the oracle (float64, NumPy) on the host over (sequence, KV head) groups of
     the same workload, in order, until ``budget_s`` seconds of oracle work or the whole
     workload is done. Widening the device data to float64 is not timed."""
-    import numpy as np
 
     from oracle import attend_rows
     from split_kv_exact_amd.metrics import visible_pairs  # noqa: F401
@@ -157,6 +158,9 @@ def main() -> int:
     ap.add_argument("--cost-ridge", type=int, default=0,
                     help="LPT unit cost: 0 = q * len * heads (the pages' cost); R > 0 = len * max(q * g, R) "
                          "per KV head (roofline-aware, R = ridge in query rows)")
+    ap.add_argument("--no-xcd-calibration", action="store_true",
+                    help="skip the calibration launches that measure the 8 XCDs' relative speeds and re-place "
+                         "the plan's workers (most loaded on the fastest XCDs) before timing")
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward pass (splitkv_attn_backward) and report it under 'backward'")
     ap.add_argument("--planner-study", action="store_true",
@@ -205,6 +209,10 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     sched = args.schedule
+    xcd_cal = None
+    if not args.no_xcd_calibration and wl.num_workers % 8 == 0:
+        print("[bench] XCD speed calibration", file=sys.stderr, flush=True)
+        plan, dev_plan, xcd_cal = _calibrate_xcd(skv, wl, plan, dev_plan, q, k, v, ws, args.cost_ridge, dev)
 
     def step():
         skv.splitkv_attn(plan, dev_plan, q, k, v, ws, out, lse, schedule=sched)
@@ -328,6 +336,7 @@ def main() -> int:
             "lower_bound": info["lower_bound"],
             "plan_ms_median": round(plan_times[len(plan_times) // 2], 4),
             "schedule": sched,
+            "xcd_calibration": xcd_cal,
             "measured_per_cu": measured,
         },
         "workspace_bytes": info["workspace_bytes"],
@@ -343,6 +352,34 @@ def main() -> int:
     return 0
 
 
+def _calibrate_xcd(skv, wl, plan, dev_plan, q, k, v, ws, ridge, dev, launches=5):
+    """Relative speeds of the 8 XCDs from static launches of the plan: each workgroup's
+    busy time on the GPU clock against its worker's planned load (workgroup w runs
+    worker w and sits on XCD w % 8). Returns the plan rebuilt with those speeds (same
+    units per worker, most loaded workers on the fastest XCDs), its device copy, and a
+    summary."""
+    import torch
+
+    m = wl.num_workers
+    load = plan.export()["load"].astype(np.float64)
+    clock = torch.zeros(2 * m, dtype=torch.int64, device=dev)
+    busy = np.zeros(m)
+    for _ in range(launches):
+        skv.splitkv_partial_attn(plan, dev_plan, q, k, v, ws, schedule="static", clock=clock)
+        torch.cuda.synchronize()
+        ck = clock.view(-1, 2).cpu().double().numpy()
+        busy += ck[:, 1] - ck[:, 0]
+    rate = np.array([load[x::8].sum() / max(busy[x::8].sum(), 1.0) for x in range(8)])
+    speeds = [max(1, int(round(1000.0 * r / rate.max()))) for r in rate]
+    plan2 = skv.plan_for(wl, ridge, speeds)
+    dev_plan2 = skv.splitkv_plan_upload(plan2, dev)
+    return plan2, dev_plan2, {
+        "launches": launches,
+        "busy_us_mean_by_xcd": [round(float(busy[x::8].mean()) / launches / 100.0, 1) for x in range(8)],
+        "xcd_speed": speeds,
+    }
+
+
 def planner_study(milp_seconds: float = 20.0):
     """The Split-KV page ("Timeline") reports LPT planning three orders of magnitude
     faster than the best load-balancing baseline, which it does not name. Here the
@@ -351,7 +388,6 @@ def planner_study(milp_seconds: float = 20.0):
     SciPy with a time limit. Instances are the first sequences of the lognormal and
     mixed workloads with fewer heads and workers, so that the MILP stays small; the
     C++ planner's time on the full workloads is reported beside them."""
-    import numpy as np
     from scipy.optimize import Bounds, LinearConstraint, milp
 
     import split_kv_exact_amd as skv

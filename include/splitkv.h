@@ -52,7 +52,7 @@ extern "C" {
 #endif
 
 #define SPLITKV_VERSION_MAJOR 0
-#define SPLITKV_VERSION_MINOR 4
+#define SPLITKV_VERSION_MINOR 5
 
 typedef enum {
   SPLITKV_OK = 0,
@@ -107,6 +107,11 @@ typedef struct {
                              * R > 0 = len * max(q_s * g, R) per KV head, i.e. a unit  *
                              * served by fewer than R query rows per KV head costs as  *
                              * streaming its block does (roofline-aware cost)          */
+  const int32_t *xcd_speed; /* NULL, or [8] relative speeds (>= 1) of the GPU's 8 XCDs  *
+                             * (workgroup w of a launch runs on XCD w % 8), e.g. from  *
+                             * the worker_clock of a calibration launch: the plan's    *
+                             * most loaded workers are then placed on workgroups of    *
+                             * the fastest XCDs. The plan itself is unchanged.         */
 } splitkv_problem;
 
 typedef struct splitkv_plan_s splitkv_plan_t; /* opaque, library-owned host object */

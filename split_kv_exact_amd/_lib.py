@@ -59,6 +59,7 @@ class Problem(ctypes.Structure):
         ("causal", ctypes.c_int32),
         ("granularity", ctypes.c_int32),
         ("cost_ridge_rows", ctypes.c_int32),
+        ("xcd_speed", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 

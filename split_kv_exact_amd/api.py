@@ -86,9 +86,12 @@ def splitkv_plan(
     causal: bool = True,
     granularity: int = L.SPLITKV_UNIT_SEQ_BLOCK_KVHEAD,
     cost_ridge_rows: int = 0,
+    xcd_speed: Sequence[int] | None = None,
 ) -> Plan:
     """Build the LPT plan on the host (``splitkv_plan``). ``cost_ridge_rows`` selects the
-    unit cost: 0 is q * len * heads, R > 0 is len * max(q * g, R) per KV head."""
+    unit cost: 0 is q * len * heads, R > 0 is len * max(q * g, R) per KV head.
+    ``xcd_speed`` (8 relative speeds, or None) places the most loaded workers on the
+    workgroups of the fastest XCDs."""
     lib = L.load()
     kv = np.ascontiguousarray(np.asarray(kv_lens, dtype=np.int64))
     ql = np.ascontiguousarray(np.asarray(q_lens, dtype=np.int32))
@@ -105,18 +108,25 @@ def splitkv_plan(
         granularity=granularity,
         cost_ridge_rows=cost_ridge_rows,
     )
+    speeds = None
+    if xcd_speed is not None:
+        speeds = np.ascontiguousarray(np.asarray(xcd_speed, dtype=np.int32))
+        if speeds.shape != (8,):
+            raise ValueError("xcd_speed must hold 8 values")
+        prob.xcd_speed = speeds.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     h = ctypes.c_void_p()
     _check(lib, lib.splitkv_plan(ctypes.byref(prob), ctypes.byref(h)), "splitkv_plan")
     problem = dict(kv_lens=kv.tolist(), q_lens=ql.tolist(), num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                    head_dim=head_dim, block_len=block_len, num_workers=num_workers, causal=bool(causal),
-                   granularity=granularity, cost_ridge_rows=cost_ridge_rows)
+                   granularity=granularity, cost_ridge_rows=cost_ridge_rows,
+                   xcd_speed=None if speeds is None else speeds.tolist())
     return Plan(h, problem, lib)
 
 
-def plan_for(wl, cost_ridge_rows: int = 0) -> Plan:
+def plan_for(wl, cost_ridge_rows: int = 0, xcd_speed: Sequence[int] | None = None) -> Plan:
     """Plan for a ``workloads.Workload``."""
     return splitkv_plan(wl.kv_lens, wl.q_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_len,
-                        wl.num_workers, wl.causal, wl.granularity, cost_ridge_rows)
+                        wl.num_workers, wl.causal, wl.granularity, cost_ridge_rows, xcd_speed)
 
 
 # --------------------------------------------------------------------------- device side

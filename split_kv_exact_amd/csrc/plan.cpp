@@ -41,6 +41,9 @@ bool validate_problem(const splitkv_problem* p, std::string* why) {
   if (p->granularity != SPLITKV_UNIT_SEQ_BLOCK_KVHEAD && p->granularity != SPLITKV_UNIT_SEQ_BLOCK)
     return fail("unknown granularity");
   if (p->cost_ridge_rows < 0 || p->cost_ridge_rows > (1 << 30)) return fail("cost_ridge_rows must be in [0, 2^30]");
+  if (p->xcd_speed)
+    for (int x = 0; x < 8; ++x)
+      if (p->xcd_speed[x] < 1) return fail("xcd_speed entries must be >= 1");
   const int64_t g = p->num_q_heads / p->num_kv_heads;
   for (int32_t s = 0; s < p->batch; ++s) {
     if (p->q_lens[s] < 1) return fail("every q_len must be >= 1");
@@ -69,6 +72,8 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   pl->causal = p->causal;
   pl->granularity = p->granularity;
   pl->ridge = p->cost_ridge_rows;
+  pl->xcd_speed.clear();
+  if (p->xcd_speed) pl->xcd_speed.assign(p->xcd_speed, p->xcd_speed + 8);
   pl->g = p->num_q_heads / p->num_kv_heads;
   pl->kv_lens.assign(p->kv_lens, p->kv_lens + p->batch);
   pl->q_lens.assign(p->q_lens, p->q_lens + p->batch);
@@ -190,6 +195,24 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
                       ? 0.0
                       : double(int64_t(m) * pl->makespan - pl->total_cost) / double(pl->total_cost);
 
+  // Placement of the plan's workers on the launch's workgroups: workgroup (slot) s runs
+  // on XCD s % 8 (workgroups are dealt to the XCDs round-robin). Without XCD speeds,
+  // slot s runs worker s. With them, the most loaded workers go to the slots of the
+  // fastest XCDs: workers by load descending and slots by their XCD's speed descending
+  // (ties by index), paired in order. The plan itself (which units each worker has)
+  // does not change.
+  pl->slot_worker.resize(m);
+  std::iota(pl->slot_worker.begin(), pl->slot_worker.end(), 0);
+  if (!pl->xcd_speed.empty()) {
+    std::vector<int32_t> ws(m), ss(m);
+    std::iota(ws.begin(), ws.end(), 0);
+    std::iota(ss.begin(), ss.end(), 0);
+    std::stable_sort(ws.begin(), ws.end(), [&](int32_t a, int32_t b) { return pl->load[a] > pl->load[b]; });
+    std::stable_sort(ss.begin(), ss.end(),
+                     [&](int32_t a, int32_t b) { return pl->xcd_speed[a % 8] > pl->xcd_speed[b % 8]; });
+    for (int32_t i = 0; i < m; ++i) pl->slot_worker[ss[i]] = ws[i];
+  }
+
   // Device image.
   ImageLayout& L = pl->layout;
   uint64_t off = 0;
@@ -276,9 +299,10 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
       for (int32_t k = 0; k < unit_njob[u]; ++k) jobs[unit_job[u] + k].flags |= kJobStream;
   for (int32_t x = 0; x < ncls; ++x) {
     std::vector<int32_t> shared;
-    typedef std::pair<int64_t, int32_t> LoadW;  // (estimated time, worker)
+    typedef std::pair<int64_t, int32_t> LoadW;  // (estimated time, slot)
     std::priority_queue<LoadW, std::vector<LoadW>, std::greater<LoadW>> heap;
-    for (int32_t w = x; w < m; w += ncls) {
+    for (int32_t sl = x; sl < m; sl += ncls) {
+      const int32_t w = pl->slot_worker[sl];
       int64_t own = 0;
       for (int32_t i = pl->worker_ptr[w]; i < pl->worker_ptr[w + 1]; ++i) {
         const int32_t u = pl->worker_units[i];
@@ -289,7 +313,7 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
             own += jc[unit_job[u] + k];
         }
       }
-      heap.push(LoadW(own, w));
+      heap.push(LoadW(own, sl));
     }
     std::sort(shared.begin(), shared.end());  // job numbers follow the LPT order
     for (int32_t jn : shared) {
@@ -299,12 +323,14 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
       e.first += jc[jn];
       heap.push(e);
     }
-    for (int32_t w = x; w < m; w += ncls)
+    for (int32_t sl = x; sl < m; sl += ncls) {
+      const int32_t w = pl->slot_worker[sl];
       for (int32_t i = pl->worker_ptr[w]; i < pl->worker_ptr[w + 1]; ++i) {
         const int32_t u = pl->worker_units[i];
         if (unit_njob[u] == 1 || ncls == 1)
-          for (int32_t k = 0; k < unit_njob[u]; ++k) lists_w[w].push_back(unit_job[u] + k);
+          for (int32_t k = 0; k < unit_njob[u]; ++k) lists_w[sl].push_back(unit_job[u] + k);
       }
+    }
   }
   std::vector<int32_t> wjobs;
   wjobs.reserve(jobs.size());
@@ -355,15 +381,22 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   pl->image.assign(L.total, 0);
   uint8_t* base = pl->image.data();
   std::memcpy(base + L.seqs, pl->seqs.data(), sizeof(SeqRec) * S);
+  // Units grouped by slot (the workers placed on the slots, in slot order).
   UnitRec* ur = reinterpret_cast<UnitRec*>(base + L.units);
-  for (int64_t i = 0; i < n; ++i) {
-    const int32_t u = pl->worker_units[i];
-    ur[i].seq = pl->u_seq[u];
-    ur[i].block = pl->u_block[u];
-    ur[i].kv0 = per_head ? pl->u_kv[u] : 0;
-    ur[i].nkv = per_head ? 1 : Hkv;
+  int32_t* sp = reinterpret_cast<int32_t*>(base + L.worker_ptr);
+  sp[0] = 0;
+  int64_t ui = 0;
+  for (int32_t sl = 0; sl < m; ++sl) {
+    const int32_t w = pl->slot_worker[sl];
+    for (int32_t i = pl->worker_ptr[w]; i < pl->worker_ptr[w + 1]; ++i, ++ui) {
+      const int32_t u = pl->worker_units[i];
+      ur[ui].seq = pl->u_seq[u];
+      ur[ui].block = pl->u_block[u];
+      ur[ui].kv0 = per_head ? pl->u_kv[u] : 0;
+      ur[ui].nkv = per_head ? 1 : Hkv;
+    }
+    sp[sl + 1] = int32_t(ui);
   }
-  std::memcpy(base + L.worker_ptr, pl->worker_ptr.data(), sizeof(int32_t) * (m + 1));
   int64_t* ma = reinterpret_cast<int64_t*>(base + L.merge_all);
   int32_t* mm = reinterpret_cast<int32_t*>(base + L.merge_multi);
   int64_t* mb = reinterpret_cast<int64_t*>(base + L.merge_multi_base);

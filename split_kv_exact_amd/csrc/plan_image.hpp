@@ -74,14 +74,14 @@ static_assert(sizeof(JobRec) == 64, "JobRec layout");
 // Offsets of the arrays inside the image.
 struct ImageLayout {
   uint64_t seqs;        // SeqRec[S]
-  uint64_t units;       // UnitRec[num_units], grouped by worker (worker order)
-  uint64_t worker_ptr;  // int32[m + 1]: worker w owns units [worker_ptr[w], worker_ptr[w+1])
+  uint64_t units;       // UnitRec[num_units], grouped by workgroup (the worker placed on it)
+  uint64_t worker_ptr;  // int32[m + 1]: workgroup w runs units [worker_ptr[w], worker_ptr[w+1])
   uint64_t merge_all;   // int64[S + 1]: prefix of Hkv * rows over all sequences
   uint64_t merge_multi; // int32[S_multi] sequence ids with nb > 1, then
   uint64_t merge_multi_base;  // int64[S_multi + 1]: prefix of Hkv * rows over them
   uint64_t jobs;        // JobRec[num_jobs] in LPT order
-  uint64_t wjobs;       // int32[num_jobs]: job indices of each worker's units, worker by worker
-  uint64_t job_ptr;     // int32[m + 1]: worker w's jobs are wjobs[job_ptr[w] .. job_ptr[w+1])
+  uint64_t wjobs;       // int32[num_jobs]: job indices of each workgroup's units, workgroup by workgroup
+  uint64_t job_ptr;     // int32[m + 1]: workgroup w's jobs are wjobs[job_ptr[w] .. job_ptr[w+1])
   uint64_t chunk_ptr;   // int32[num_chunks + 1]: the shared tail's chunks of consecutive jobs
   uint64_t sched;       // kSchedBytes, 256-byte aligned: counters of the shared job queue
   uint64_t total;

@@ -40,13 +40,18 @@ def test_version_and_status_strings(lib):
     assert lib.splitkv_status_string(-99) == b"unknown status"
 
 
-def _problem(kv, q, hq=4, hkv=2, d=128, b=64, m=8, causal=1, gran=0, ridge=0):
+def _problem(kv, q, hq=4, hkv=2, d=128, b=64, m=8, causal=1, gran=0, ridge=0, speeds=None):
     kv = np.asarray(kv, np.int64)
     q = np.asarray(q, np.int32)
     p = L.Problem(batch=len(kv), kv_lens=kv.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                   q_lens=q.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), num_q_heads=hq, num_kv_heads=hkv,
                   head_dim=d, block_len=b, num_workers=m, causal=causal, granularity=gran, cost_ridge_rows=ridge)
-    return p, (kv, q)
+    keep = (kv, q)
+    if speeds is not None:
+        sp = np.asarray(speeds, np.int32)
+        p.xcd_speed = sp.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        keep = (kv, q, sp)
+    return p, keep
 
 
 @pytest.mark.parametrize("kw", [
@@ -57,6 +62,7 @@ def _problem(kv, q, hq=4, hkv=2, d=128, b=64, m=8, causal=1, gran=0, ridge=0):
     dict(kv=[10], q=[2], m=0),       # num_workers < 1
     dict(kv=[10], q=[2], causal=2),
     dict(kv=[10], q=[2], gran=7),
+    dict(kv=[10], q=[2], speeds=[1, 1, 1, 0, 1, 1, 1, 1]),  # an XCD speed below 1
     dict(kv=[10], q=[2], ridge=-1),  # negative ridge
     dict(kv=[10], q=[2], ridge=(1 << 30) + 1),
     dict(kv=[1 << 40], q=[1 << 20], hq=1024, hkv=1, b=1 << 30),  # total cost beyond 2^62

@@ -134,13 +134,16 @@ def test_repeated_calls_reuse_buffers():
 
 
 def _schedules_agree(wl, q, k, v, m=None):
-    """Partials and fused outputs under every job schedule, and under a plan built with
-    the roofline-aware cost (other placement, same jobs), bit for bit; afterwards the
-    plan buffers' scheduling areas (their last 1024 bytes) are zero again."""
+    """Partials and fused outputs under every job schedule, under a plan built with the
+    roofline-aware cost (other placement, same jobs), and under one whose workers are
+    re-placed by XCD speeds, bit for bit; afterwards the plan buffers' scheduling areas
+    (their last 1024 bytes) are zero again."""
     w = wl if m is None else wl.with_workers(m)
     res = {}
-    for ridge, scheds in ((0, ("static", "queue", "queue", "auto")), (128, ("static", "queue"))):
-        plan = skv.plan_for(w, ridge)
+    speeds = [1000, 900, 1000, 970, 1000, 910, 990, 1000]
+    for ridge, sp, scheds in ((0, None, ("static", "queue", "queue", "auto")), (128, None, ("static", "queue")),
+                              (0, speeds, ("static", "queue"))):
+        plan = skv.plan_for(w, ridge, sp)
         dev_plan = skv.splitkv_plan_upload(plan)
         for sched in scheds:
             ws = skv.workspace(plan)
@@ -148,10 +151,10 @@ def _schedules_agree(wl, q, k, v, m=None):
             skv.splitkv_partial_attn(plan, dev_plan, q, k, v, ws, schedule=sched)
             out, lse = skv.splitkv_attn(plan, dev_plan, q, k, v, schedule=sched)
             wo, wlse = skv.workspace_views(plan, ws)
-            res.setdefault((ridge, sched), []).append((wo, wlse, out, lse))
+            res.setdefault((ridge, sp is not None, sched), []).append((wo, wlse, out, lse))
         torch.cuda.synchronize()
         assert int(dev_plan[-1024:].count_nonzero()) == 0, "scheduling area not left zero"
-    ref = res[(0, "static")][0]
+    ref = res[(0, False, "static")][0]
     assert not torch.isnan(ref[1]).any()
     for key, runs in res.items():
         for got in runs:
@@ -165,6 +168,26 @@ def test_static_and_queue_schedules_agree(wl):
     say(f"[gpu] schedules on {wl.name}")
     q, k, v = make_qkv(wl, "cuda")
     _schedules_agree(wl, q, k, v)
+
+
+def test_xcd_placement_fp32_agrees():
+    """The float32 kernel walks each workgroup's units; re-placed workers give the same
+    partials bit for bit."""
+    for wl in [w for w in SMALL if w.dtype == "float32"]:
+        say(f"[gpu] XCD placement on {wl.name}")
+        q, k, v = make_qkv(wl, "cuda")
+        got = []
+        for sp in (None, [1000, 1, 500, 999, 1000, 2, 800, 1000]):
+            plan = skv.plan_for(wl, 0, sp)
+            dev_plan = skv.splitkv_plan_upload(plan)
+            ws = skv.workspace(plan)
+            ws.fill_(float("nan"))
+            skv.splitkv_partial_attn(plan, dev_plan, q, k, v, ws)
+            out, lse = skv.splitkv_attn(plan, dev_plan, q, k, v)
+            got.append((*skv.workspace_views(plan, ws), out, lse))
+        torch.cuda.synchronize()
+        for a, b in zip(*got):
+            assert torch.equal(a, b)
 
 
 def test_worker_clock():

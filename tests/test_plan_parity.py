@@ -58,3 +58,17 @@ def test_random_instances_bit_exact():
 def test_worker_count_larger_than_units():
     inf = compare([10], [2], 2, 1, 4, 64)
     assert inf["makespan"] == inf["lower_bound"]
+
+
+def test_xcd_speeds_leave_the_plan_unchanged():
+    """Speeds only place workers on workgroups: the exported LPT plan is identical."""
+    wl = get_workload("batch8")
+    a = skv_plan(wl, None)
+    b = skv_plan(wl, [1000, 920, 1000, 980, 1000, 920, 1000, 980])
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+def skv_plan(wl, speeds):
+    from split_kv_exact_amd import plan_for
+    return plan_for(wl, 0, speeds).export()
