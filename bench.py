@@ -158,6 +158,9 @@ def main() -> int:
     ap.add_argument("--cost-ridge", type=int, default=0,
                     help="LPT unit cost: 0 = q * len * heads (the pages' cost); R > 0 = len * max(q * g, R) "
                          "per KV head (roofline-aware, R = ridge in query rows)")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed fused steps for this long before the warmup steps (the GPU's clocks ramp up "
+                         "over the first tens of milliseconds of work)")
     ap.add_argument("--no-xcd-calibration", action="store_true",
                     help="skip the calibration launches that measure the 8 XCDs' relative speeds and re-place "
                          "the plan's workers (most loaded on the fastest XCDs) before timing")
@@ -230,7 +233,14 @@ def main() -> int:
         dst.copy_(src)  # reads 1 GiB, writes 1 GiB
         torch.cuda.synchronize()
         del src, dst
-    print("[bench] warmup", file=sys.stderr, flush=True)
+    print("[bench] settle and warmup", file=sys.stderr, flush=True)
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_ms * 1e-3:
+        for _ in range(4):
+            step()
+        settle_steps += 4
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -325,6 +335,7 @@ def main() -> int:
         "ms_merge_kernel": round(ms_merge, 5),
         "ms_per_step_cold_cache": None if ms_cold is None else round(ms_cold, 5),
         "wall_ms_per_step": round(wall_ms, 5),
+        "settle": {"ms": args.settle_ms, "steps": settle_steps},
         "effective_bytes": eb,
         "flops": fl,
         "lpt": {

@@ -18,6 +18,9 @@
 //     a stage sits at a fixed offset from the stage's base address, so issuing a
 //     stage costs one scalar add per tensor; only a block's last, partial stage
 //     computes clamped offsets.
+//   * Only waves 4..7 issue the DMA. Issuing a stage's 32 KiB queues behind the
+//     memory pipeline for hundreds of cycles; waves 0..3, which compute every job,
+//     never wait there (jobs of fewer than 8 row tiles compute on waves 0..3 alone).
 //   * Each stage costs one workgroup barrier. Completion of a stage's DMA is tracked
 //     with explicit vmcnt waits: vector-memory instructions complete in issue order,
 //     and the kernel counts every one it issues after a stage (the next stage's DMA
@@ -28,9 +31,10 @@
 //     conflicts and so that a lane's read offsets do not depend on the stage.
 //   * Query rows of a KV head are r = i*g + (h - kv*g) (query token i, head h), in
 //     16-row tiles. With >= 8 tiles the 8 waves split the tiles (up to 2 each, so 256
-//     rows per pass); with fewer tiles the waves also split each stage's keys two ways
-//     and merge their results in LDS at the end of the job. Rows past the last query
-//     row repeat the last row, so every wave stores whole tiles.
+//     rows per pass); with 4..7 tiles waves 0..3 split them; with 1..3 tiles waves
+//     split the tiles and each stage's keys two ways and merge their results in LDS at
+//     the end of the job. Rows past the last query row repeat the last row, so every
+//     wave stores whole tiles.
 //   * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16, A = 16
 //     keys x 32 dims from the K tile, B = 32 dims x 16 rows of Q in registers). A lane
 //     then owns one query row and 4 keys per 16-key tile: the row max needs two
@@ -57,6 +61,7 @@ constexpr int NW = 8;           // wavefronts per workgroup (two per SIMD)
 constexpr int TK = kStageKeys;  // keys per pipeline stage
 constexpr int NST = 3;          // pipeline slots
 constexpr int RTW = 2;          // row tiles per wave per pass
+constexpr int NLW = 4;          // loader waves: waves NW - NLW .. NW - 1 issue all DMA
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.69314718055994531f;
 constexpr float NEG_INF = -__builtin_huge_valf();
@@ -73,8 +78,8 @@ struct Cfg {
   static constexpr int TILEB = TK * ROWB;            // bytes of a K or V tile
   static constexpr int QTILEB = kQTileRows * ROWB;   // bytes of a Q tile
   static constexpr int SLOTB = 2 * TILEB + QTILEB;   // bytes per pipeline slot
-  static constexpr int KV_INST = TILEB / 1024 / NW;  // DMA instructions per wave per K (or V) tile
-  static constexpr int Q_INST = QTILEB / 1024 / NW;  // DMA instructions per wave per Q tile
+  static constexpr int KV_INST = TILEB / 1024 / NLW;  // DMA instructions per loader wave per K (or V) tile
+  static constexpr int Q_INST = QTILEB / 1024 / NLW;  // DMA instructions per loader wave per Q tile
   static constexpr int MSLOT = 64 * (DT * 4 + 3);    // floats of one merge record (m, l, ls, O)
   static constexpr int STORES = DT + 1;              // store instructions per finished row tile
   // At least 96 KiB so that a compute unit holds a single workgroup.
@@ -145,14 +150,18 @@ struct LaneOff {
   uint32_t vr[Cfg<D>::DT];       // LDS: V^T operand (key row 4G + li/4, dims 16dt + 4(li%4)..+3)
 };
 
+// Loader wave index (0..NLW-1), or -1 for a wave that issues no DMA.
+__device__ __forceinline__ int loader_index(int wave) { return wave >= NW - NLW ? wave - (NW - NLW) : -1; }
+
 template <int D>
 __device__ __forceinline__ void lane_offsets(LaneOff<D>& lo, int wave, int lane, uint32_t kst, uint32_t vst) {
   using C = Cfg<D>;
   const int G = lane >> 4, li = lane & 15;
   const int cs = lane % C::CH;
+  const int lw = max(loader_index(wave), 0);
 #pragma unroll
   for (int in = 0; in < C::KV_INST; ++in) {
-    const int row = (wave * C::KV_INST + in) * C::RPI + lane / C::CH;
+    const int row = (lw * C::KV_INST + in) * C::RPI + lane / C::CH;
     lo.dk[in] = uint32_t(row) * kst + 16u * swz_k<D>(row, cs);
     lo.dv[in] = uint32_t(row) * vst + 16u * swz_v<D>(row, cs);
   }
@@ -187,11 +196,13 @@ template <int D, int AUX>
 __device__ __forceinline__ void issue_kv(const Loader& L, unsigned char* slot, const LaneOff<D>& lo, int wave,
                                          int lane, uint32_t kst, uint32_t vst) {
   using C = Cfg<D>;
+  const int lw = loader_index(wave);
+  if (lw < 0) return;
   const int rem = L.len - L.stage * TK;  // keys of the block from this stage's first key on
   if (rem >= TK) {
 #pragma unroll
     for (int in = 0; in < C::KV_INST; ++in) {
-      const int gi = wave * C::KV_INST + in;
+      const int gi = lw * C::KV_INST + in;
       __builtin_amdgcn_global_load_lds(L.kb + lo.dk[in], (lds_void*)(slot + gi * 1024), 16, 0, AUX);
       __builtin_amdgcn_global_load_lds(L.vb + lo.dv[in], (lds_void*)(slot + C::TILEB + gi * 1024), 16, 0, AUX);
     }
@@ -201,7 +212,7 @@ __device__ __forceinline__ void issue_kv(const Loader& L, unsigned char* slot, c
     const int cs = lane % C::CH;
 #pragma unroll
     for (int in = 0; in < C::KV_INST; ++in) {
-      const int gi = wave * C::KV_INST + in;
+      const int gi = lw * C::KV_INST + in;
       const int row = gi * C::RPI + lane / C::CH;
       const uint32_t t = uint32_t(min(row, rem - 1));
       __builtin_amdgcn_global_load_lds(L.kb + (t * kst + 16u * swz_k<D>(row, cs)), (lds_void*)(slot + gi * 1024),
@@ -212,8 +223,9 @@ __device__ __forceinline__ void issue_kv(const Loader& L, unsigned char* slot, c
   }
 }
 
-// Issue the DMA of the loader's next stage into one pipeline slot and advance the
-// loader; returns the number of vector-memory instructions this wave issued.
+// Issue the DMA of the loader's next stage into one pipeline slot (loader waves) and
+// advance the loader (every wave); returns the number of vector-memory instructions
+// this wave issued.
 template <int D>
 __device__ __forceinline__ int issue_stage(const PartialArgs& a, const JobRec* __restrict__ jobs, Loader& L,
                                            unsigned char* slot, const LaneOff<D>& lo, int wave, int lane,
@@ -223,8 +235,9 @@ __device__ __forceinline__ int issue_stage(const PartialArgs& a, const JobRec* _
     issue_kv<D, 2>(L, slot, lo, wave, lane, kst, vst);
   else
     issue_kv<D, 0>(L, slot, lo, wave, lane, kst, vst);
-  int n = 2 * C::KV_INST;
-  if (L.stage == 0 && (L.flags & kJobQTile)) {
+  const int lw = loader_index(wave);
+  int n = lw >= 0 ? 2 * C::KV_INST : 0;
+  if (L.stage == 0 && (L.flags & kJobQTile) && lw >= 0) {
     // The job's query rows (at most 64) ride with its first stage; rows past the last
     // one repeat it.
     const JobRec j = jobs[L.job];
@@ -234,7 +247,7 @@ __device__ __forceinline__ int issue_stage(const PartialArgs& a, const JobRec* _
     const int cs = lane % C::CH;
 #pragma unroll
     for (int in = 0; in < C::Q_INST; ++in) {
-      const int gi = wave * C::Q_INST + in;
+      const int gi = lw * C::Q_INST + in;
       const int row = gi * C::RPI + lane / C::CH;
       const int rr = min(row, j.rows - 1);
       const int i = rr / a.g, hl = rr - i * a.g;
@@ -267,9 +280,10 @@ __device__ __forceinline__ int tile_row(const JobRec& j, int tile, int li) { ret
 __device__ __forceinline__ void open_work(Work& w, const JobRec& j, int wave, int g) {
   w.nst = j.nst;
   // Waves split the row tiles 2^wr_log ways and each stage's keys Wk ways
-  // (2^wr_log * Wk <= NW; the other waves only load).
+  // (2^wr_log * Wk <= NW; the other waves compute nothing in this job). With 4..7
+  // tiles only waves 0..3 compute, so that the loader waves 4..7 stay free.
   w.wr_log = j.flags & kJobWrMask;
-  w.Wk = w.wr_log == 3 ? 1 : 2;
+  w.Wk = w.wr_log >= 2 ? 1 : 2;
   const int Wr = 1 << w.wr_log;
   w.rg = wave & (Wr - 1);
   w.ks = wave >> w.wr_log;
