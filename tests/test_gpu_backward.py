@@ -48,6 +48,7 @@ CASES = [
     _wl("single_block", [100, 37], [3, 2], 8, 2, 128, 4096, 4),
     _wl("two_row_passes", [2048], [300], 32, 8, 128, 512, 8),
     _wl("boosted_keys", [3000, 1500], [16, 1], 64, 8, 128, 512, 32, boost_frac=0.01),
+    _wl("mid_tiles", [700, 1200, 333], [5, 6, 7], 32, 2, 128, 256, 9),
 ]
 
 

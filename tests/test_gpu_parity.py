@@ -51,6 +51,9 @@ SMALL = [
     # Multi-job units dealt over the workers of an XCD class (needs >= 16 workers).
     _wl("multi_pass_dealt", [2048, 900, 5000], [300, 70, 16], 32, 8, 128, 512, 32),
     _wl("whole_block_dealt", [900, 260, 3000], [8, 2, 33], 16, 4, 128, 256, 16, gran=1),
+    # 5, 6 and 7 row tiles per job (GQA group 16): waves 0-3 hold one or two tiles each.
+    _wl("mid_tiles_d128", [700, 1200, 333], [5, 6, 7], 32, 2, 128, 256, 9),
+    _wl("mid_tiles_d64", [700, 1200, 333], [5, 6, 7], 32, 2, 64, 128, 9),
 ]
 
 
