@@ -8,9 +8,9 @@
 //
 // Layout of the work: lane b holds LSE_b (64 blocks at a time), so M and sum_b w_b are
 // wave reductions; the output row is then accumulated in block order, each lane owning
-// head_dim/64 dimensions, with the loads of 8 blocks issued before they are used. Block
-// order is fixed, so the result does not depend on how the plan spread the blocks
-// over workers.
+// head_dim/64 dimensions, with the loads of 16 blocks issued before they are used (the
+// first 16 before the maximum is formed). Block order is fixed, so the result does not
+// depend on how the plan spread the blocks over workers.
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
@@ -22,7 +22,7 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.69314718055994531f;
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr int WAVES = 4;
-constexpr int UNROLL = 8;
+constexpr int UNROLL = 16;
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -41,14 +41,14 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int64_t gw = int64_t(blockIdx.x) * WAVES + (threadIdx.x >> 6);
   if (gw >= a.total_rows) return;
   const int lane = threadIdx.x & 63;
-  // Sequence j with row_base[j] <= gw < row_base[j + 1].
-  int lo = 0, hi = a.count - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.row_base[mid] <= gw)
-      lo = mid;
-    else
-      hi = mid - 1;
+  // Sequence j with row_base[j] <= gw < row_base[j + 1]: row_base is non-decreasing, so
+  // the entries <= gw form a prefix; lanes test 64 entries per load.
+  int lo = 0;
+  for (int c0 = 0; c0 < a.count; c0 += 64) {
+    const int j = c0 + lane;
+    const uint64_t le = __ballot(j < a.count && a.row_base[j] <= gw);
+    if (le) lo = c0 + 63 - __builtin_clzll(le);
+    if (le != ~uint64_t(0)) break;
   }
   const int s = a.seq_ids ? a.seq_ids[lo] : lo;
   const SeqRec sq = a.seqs[s];
@@ -60,7 +60,19 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int64_t r0 = sq.row_base + int64_t(kv) * nb * sq.rows + r;  // block b: r0 + b * rows
   const int64_t rs = sq.rows;
 
-  // M = max_b LSE_b, then W = sum_b e^(LSE_b - M), lanes over blocks.
+  // M = max_b LSE_b, then W = sum_b e^(LSE_b - M), lanes over blocks. The first blocks'
+  // rows are requested before the maximum is formed (they do not depend on it).
+  float v[UNROLL][DPL];
+  auto load = [&](int b0, int j0, int cnt) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int jb = min(j0 + u, cnt - 1);
+      const float* ob = a.ws_o + (r0 + (b0 + jb) * rs) * D;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) v[u][k] = ob[lane + 64 * k];
+    }
+  };
+  load(0, 0, min(64, nb));
   float M = NEG_INF;
   for (int b0 = 0; b0 < nb; b0 += 64) {
     const int b = b0 + lane;
@@ -78,14 +90,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
       W += wl;
       const int cnt = min(64, nb - b0);
       for (int j0 = 0; j0 < cnt; j0 += UNROLL) {
-        float v[UNROLL][DPL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-          const int jb = min(j0 + u, cnt - 1);
-          const float* ob = a.ws_o + (r0 + (b0 + jb) * rs) * D;
-#pragma unroll
-          for (int k = 0; k < DPL; ++k) v[u][k] = ob[lane + 64 * k];
-        }
+        if (b0 > 0 || j0 > 0) load(b0, j0, cnt);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
           if (j0 + u < cnt) {
