@@ -16,6 +16,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -29,11 +30,16 @@ METRIC = "split-KV attention+merge effective HBM GB/s & TFLOP/s, % of MI355X roo
 
 
 def _kernel_sha() -> str:
+    """Hash of the forward path's sources with comments and blank space removed, so that
+    an edit of comments alone does not mark the committed counter runs as stale."""
     h = hashlib.sha256()
     for f in ("partial_bf16.hip", "partial_f32.hip", "merge.hip", "abi.cpp", "plan.cpp", "kernels.hpp",
               "plan_image.hpp", "lds_tiles.hpp"):
-        with open(os.path.join(ROOT, "split_kv_exact_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "split_kv_exact_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

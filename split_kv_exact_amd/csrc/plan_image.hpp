@@ -47,7 +47,7 @@ constexpr int32_t kSchedStride = 16;  // uint32 words between counters
 constexpr uint64_t kSchedBytes = 1024;
 
 // Job flags.
-constexpr int32_t kJobWrMask = 3;   // log2 of the row groups the 8 wavefronts form
+constexpr int32_t kJobWrMask = 3;   // log2 of the row groups the computing wavefronts form
 constexpr int32_t kJobQTile = 4;    // Q rows of the job travel through LDS with stage 0
 constexpr int32_t kJobSingle = 8;   // the sequence has a single block (its result is final)
 constexpr int32_t kJobStream = 16;  // K/V read with the non-temporal hint (the block is not read again later)
