@@ -29,13 +29,17 @@ if ROOT not in sys.path:
 METRIC = "split-KV attention+merge effective HBM GB/s & TFLOP/s, % of MI355X roofline"
 
 
-def _kernel_sha() -> str:
+KERNEL_SOURCES = ("partial_bf16.hip", "partial_f32.hip", "merge.hip", "abi.cpp", "plan.cpp", "kernels.hpp",
+                  "plan_image.hpp", "lds_tiles.hpp")
+
+
+def _kernel_sha(csrc: str | None = None) -> str:
     """Hash of the forward path's sources with comments and blank space removed, so that
     an edit of comments alone does not mark the committed counter runs as stale."""
+    csrc = csrc or os.path.join(ROOT, "split_kv_exact_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("partial_bf16.hip", "partial_f32.hip", "merge.hip", "abi.cpp", "plan.cpp", "kernels.hpp",
-              "plan_image.hpp", "lds_tiles.hpp"):
-        with open(os.path.join(ROOT, "split_kv_exact_amd", "csrc", f), encoding="utf-8") as fh:
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
