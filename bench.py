@@ -189,7 +189,7 @@ def main() -> int:
         return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: split-KV here runs on the 256 CUs of a single MI355X; "
-              "multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+              "this benchmark has no multi-GPU mode (use --gpus 1).", file=sys.stderr)
         return 2
 
     import torch
