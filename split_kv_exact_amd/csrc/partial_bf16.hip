@@ -344,17 +344,10 @@ struct Scores {
   f32x4 s[RTW][NT];
 };
 
-#ifdef SKV_SETPRIO
-#define SKV_PRIO(x) __builtin_amdgcn_s_setprio(x)
-#else
-#define SKV_PRIO(x) ((void)0)
-#endif
-
 // S^T = K Q^T for each 16-key tile, shared K operands across the row tiles.
 template <int D, int KOFF>
 __device__ __forceinline__ void step_scores(Scores<D>& S, const State<D>& st, int nt, const unsigned (&ka)[Cfg<D>::DC]) {
   using C = Cfg<D>;
-  SKV_PRIO(1);
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
     bf16x8 kop[C::DC];
@@ -371,7 +364,6 @@ __device__ __forceinline__ void step_scores(Scores<D>& S, const State<D>& st, in
       }
     }
   }
-  SKV_PRIO(0);
 }
 
 // Mask, running max, p = 2^(s*c - m*c) rounded to bf16 for the P V product; the row
@@ -440,7 +432,6 @@ __device__ __forceinline__ void step_pv(State<D>& st, int nt, const bf16x4 (&p)[
     vop[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[dt], hi[dt], 0, 1, 2, 3, 4, 5, 6, 7));
   const __bf16 one = (__bf16)1.0f;
   const bf16x8 ones = {one, one, one, one, one, one, one, one};
-  SKV_PRIO(1);
 #pragma unroll
   for (int t = 0; t < RTW; ++t) {
     if (t < nt) {
@@ -451,7 +442,6 @@ __device__ __forceinline__ void step_pv(State<D>& st, int nt, const bf16x4 (&p)[
       st.ls[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, st.ls[t], 0, 0, 0);
     }
   }
-  SKV_PRIO(0);
 }
 
 // The wave's keys of one stage: 32 keys (one step) or 64 (two steps, interleaved).
