@@ -20,9 +20,10 @@
 //            (one wavefront per row);
 //   dkv:     one workgroup of 4 waves per (sequence, KV head, 64-key tile); a wave holds
 //            its 16 keys' K and V rows in registers and dK^T, dV^T accumulators, and the
-//            query rows that see the tile stream through LDS 32 at a time: S = Q K^T,
-//            dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS with Q^T and dO^T read by
-//            transposing loads. dK and dV are written once.
+//            query rows that see the tile stream through LDS 32 at a time (direct
+//            global->LDS DMA, one chunk ahead): S = Q K^T, dP = dO V^T, then dV^T += dO^T P
+//            and dK^T += Q^T dS with Q^T and dO^T read by transposing loads. Kept at 160
+//            VGPRs or fewer (three workgroups per CU). dK and dV are written once.
 // P and dS enter the matrix cores rounded to bf16 (as P does in the forward); all sums
 // are fp32.
 #include <hip/hip_runtime.h>
@@ -298,7 +299,7 @@ struct KvLds {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 3) void dkv_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = BCfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[sizeof(KvLds<D>)];
@@ -345,10 +346,14 @@ __global__ __launch_bounds__(256) void dkv_kernel(BwdArgs a) {
   const int r_begin = int(i0) * a.g;
   const int nchunk = r_begin < rows ? (rows - r_begin + RCH - 1) / RCH : 0;
 
-  // Chunk loads: Q and dO rows as 16-byte chunks (row = cidx / CH), 256 threads.
-  constexpr int NCH = RCH * C::CH;
-  constexpr int PER = (NCH + 255) / 256;
-  u32x4 rq[PER], rg[PER];
+  // Chunk loads: Q and dO rows go straight to LDS (global_load_lds_dwordx4, 1 KiB per
+  // instruction, lane l to byte 16 l of it). LDS position p of a tile (16-byte units)
+  // is row p / CH, slot p % CH; the slot holds the row's chunk swz_tr(row, slot) (the
+  // swizzle is an XOR, its own inverse), so each lane loads the chunk its position
+  // needs. The per-row LSE, D and position travel through registers (threads < RCH).
+  constexpr int TILE_INST = RCH * C::ROWB / 1024;      // instructions per tile
+  constexpr int PER_WAVE = TILE_INST / KV_WAVES;       // per wave, per tensor
+  static_assert(PER_WAVE * KV_WAVES == TILE_INST, "chunk tile split");
   float r_l = 0.f, r_d = 0.f;
   int r_p = 0;
   auto row_src = [&](int r, int64_t& tok, int64_t& head) {
@@ -356,40 +361,34 @@ __global__ __launch_bounds__(256) void dkv_kernel(BwdArgs a) {
     tok = sq.q_base + i;
     head = int64_t(kv) * a.g + hl;
   };
-  auto load_chunk = [&](int ch) {
+  auto load_chunk = [&](int ch, int buf) {
     const int rb = r_begin + ch * RCH;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int cidx = threadIdx.x + 256 * u;
-      const int r = min(rb + cidx / C::CH, rows - 1);
-      const int cc = cidx % C::CH;
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int gi = wave * PER_WAVE + u;
+      const int p = gi * 64 + lane;
+      const int row = p / C::CH, slot = p % C::CH;
+      const int cc = swz_tr<C::CH>(row, slot);
+      const int r = min(rb + row, rows - 1);
       int64_t tok, head;
       row_src(r, tok, head);
-      rq[u] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(a.q) + 2 * (tok * a.q_st + head * a.q_sh) + 16 * cc);
-      rg[u] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(a.dout) + 2 * (tok * a.do_st + head * a.do_sh) + 16 * cc);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char*>(a.q) + 2 * (tok * a.q_st + head * a.q_sh) + 16 * cc,
+                                       (lds_void*)(L.q[buf] + gi * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char*>(a.dout) + 2 * (tok * a.do_st + head * a.do_sh) + 16 * cc,
+                                       (lds_void*)(L.g[buf] + gi * 1024), 16, 0, 0);
     }
     if (threadIdx.x < RCH) {
       const int r = rb + threadIdx.x;
       int64_t tok, head;
       row_src(min(r, rows - 1), tok, head);
-      r_l = r < rows ? a.lse[tok * a.Hq + head] * LOG2E : __builtin_huge_valf();
+      r_l = a.lse[tok * a.Hq + head];  // scaled when stored: no use of the loaded value before then
       r_d = a.ws_d[tok * a.Hq + head];
-      r_p = int(n - q + (min(r, rows - 1) / a.g));
+      r_p = r < rows ? int(n - q + (min(r, rows - 1) / a.g)) : -1;
     }
   };
   auto store_chunk = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int cidx = threadIdx.x + 256 * u;
-      if (cidx < NCH) {
-        const int row = cidx / C::CH, cc = cidx % C::CH;
-        const int off = row * C::ROWB + 16 * swz_tr<C::CH>(row, cc);
-        *reinterpret_cast<u32x4*>(L.q[buf] + off) = rq[u];
-        *reinterpret_cast<u32x4*>(L.g[buf] + off) = rg[u];
-      }
-    }
     if (threadIdx.x < RCH) {
-      L.lsec[buf][threadIdx.x] = r_l;
+      L.lsec[buf][threadIdx.x] = r_p >= 0 ? r_l * LOG2E : __builtin_huge_valf();
       L.dd[buf][threadIdx.x] = r_d;
       L.pos[buf][threadIdx.x] = r_p;
     }
@@ -405,30 +404,34 @@ __global__ __launch_bounds__(256) void dkv_kernel(BwdArgs a) {
     for (int dt = 0; dt < C::DT; ++dt) o_tr[dt] = r * C::ROWB + 16 * swz_tr<C::CH>(r, 2 * dt + (cc >> 1)) + 8 * (cc & 1);
   }
 
-  if (nchunk > 0) load_chunk(0);
+  if (nchunk > 0) load_chunk(0, 0);
   for (int ch = 0; ch < nchunk; ++ch) {
     const int buf = ch & 1;
     store_chunk(buf);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's part of chunk ch has landed
     __syncthreads();
-    if (ch + 1 < nchunk) load_chunk(ch + 1);
+    if (ch + 1 < nchunk) load_chunk(ch + 1, buf ^ 1);
     const unsigned qb = lds_addr(L.q[buf]), gb = lds_addr(L.g[buf]);
     // S and dP for the chunk's two 16-row tiles (lane: key li, rows 16 t + 4 G + e).
     f32x4 sv[2], pv[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      bf16x8 qa[C::DC], ga[C::DC];
+      bf16x8 qa[C::DC];
 #pragma unroll
-      for (int dc = 0; dc < C::DC; ++dc) {
-        qa[dc] = *reinterpret_cast<lds_bf16x8>(uintptr_t(qb + unsigned(16 * t) * C::ROWB + o_row[dc]));
-        ga[dc] = *reinterpret_cast<lds_bf16x8>(uintptr_t(gb + unsigned(16 * t) * C::ROWB + o_row[dc]));
-      }
-      f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+      for (int dc = 0; dc < C::DC; ++dc) qa[dc] = *reinterpret_cast<lds_bf16x8>(uintptr_t(qb + unsigned(16 * t) * C::ROWB + o_row[dc]));
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dc = 0; dc < C::DC; ++dc) {
-        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[dc], kt[dc], x, 0, 0, 0);
-        y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[dc], vt[dc], y, 0, 0, 0);
-      }
+      for (int dc = 0; dc < C::DC; ++dc) x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[dc], kt[dc], x, 0, 0, 0);
       sv[t] = x;
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf16x8 ga[C::DC];
+#pragma unroll
+      for (int dc = 0; dc < C::DC; ++dc) ga[dc] = *reinterpret_cast<lds_bf16x8>(uintptr_t(gb + unsigned(16 * t) * C::ROWB + o_row[dc]));
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dc = 0; dc < C::DC; ++dc) y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[dc], vt[dc], y, 0, 0, 0);
       pv[t] = y;
     }
     // P and dS (rows past the last have LSE = +inf, so P = 0).
@@ -447,27 +450,31 @@ __global__ __launch_bounds__(256) void dkv_kernel(BwdArgs a) {
     const bf16x8 db = {(__bf16)ds[0][0], (__bf16)ds[0][1], (__bf16)ds[0][2], (__bf16)ds[0][3],
                        (__bf16)ds[1][0], (__bf16)ds[1][1], (__bf16)ds[1][2], (__bf16)ds[1][3]};
     // dV^T += dO^T P and dK^T += Q^T dS over the chunk's 32 rows.
-    {
-      unsigned ga[C::DT];
+    // In halves of D/32 dimension tiles, to keep the transposed operands few.
+    constexpr int DH = C::DT / 2;
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) ga[dt] = gb + o_tr[dt];
-      i16x4 lo[C::DT], hi[C::DT];
+    for (int half = 0; half < 2; ++half) {
+      unsigned ga[DH];
+#pragma unroll
+      for (int d = 0; d < DH; ++d) ga[d] = gb + o_tr[half * DH + d];
+      i16x4 lo[DH], hi[DH];
       tr_read<0, 16 * C::ROWB>(lo, hi, ga);
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
-        dv[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[dt], hi[dt], 0, 1, 2, 3, 4, 5, 6, 7)), pb, dv[dt], 0, 0, 0);
+      for (int d = 0; d < DH; ++d)
+        dv[half * DH + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[d], hi[d], 0, 1, 2, 3, 4, 5, 6, 7)), pb, dv[half * DH + d], 0, 0, 0);
     }
-    {
-      unsigned qa[C::DT];
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) qa[dt] = qb + o_tr[dt];
-      i16x4 lo[C::DT], hi[C::DT];
+    for (int half = 0; half < 2; ++half) {
+      unsigned qa[DH];
+#pragma unroll
+      for (int d = 0; d < DH; ++d) qa[d] = qb + o_tr[half * DH + d];
+      i16x4 lo[DH], hi[DH];
       tr_read<0, 16 * C::ROWB>(lo, hi, qa);
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
-        dk[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[dt], hi[dt], 0, 1, 2, 3, 4, 5, 6, 7)), db, dk[dt], 0, 0, 0);
+      for (int d = 0; d < DH; ++d)
+        dk[half * DH + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[d], hi[d], 0, 1, 2, 3, 4, 5, 6, 7)), db, dk[half * DH + d], 0, 0, 0);
     }
     __syncthreads();  // every wave is done with this buffer before it is refilled
   }

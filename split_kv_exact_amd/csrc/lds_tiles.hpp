@@ -63,6 +63,15 @@ __device__ __forceinline__ void tr_read(i16x4 (&lo)[4], i16x4 (&hi)[4], const un
         "=&v"(hi[3])
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF), "i"(OFF + HI));
 }
+template <int OFF, int HI>
+__device__ __forceinline__ void tr_read(i16x4 (&lo)[2], i16x4 (&hi)[2], const unsigned (&a)[2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%6\n\tds_read_b64_tr_b16 %1, %5 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %2, %4 offset:%7\n\tds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(hi[0]), "=&v"(hi[1])
+      : "v"(a[0]), "v"(a[1]), "i"(OFF), "i"(OFF + HI));
+}
 
 }  // namespace lds
 }  // namespace splitkv
