@@ -11,7 +11,8 @@
 // The page describes no kernel; this is a CDNA4 design in four launches:
 //   rowdot:  D_i = <dO_i, O_i> for every query row (one wavefront per row);
 //   dq:      one workgroup per forward job (a unit's KV head and up to 256 of its query
-//            rows): its block's keys stream through LDS in stages of 32; each wave keeps
+//            rows): its block's keys stream through LDS in stages of 32 (direct
+//            global->LDS DMA, three stages in flight); each wave keeps
 //            Q, dO and its dQ part of two 16-row tiles in registers. Scores are computed
 //            transposed as in the forward (S^T = K Q^T), dP^T = V dO^T the same way, and
 //            dQ^T += K^T dS^T with K^T read by transposing LDS loads. The part goes to the
@@ -76,11 +77,23 @@ constexpr int RT = 2;  // row tiles per wave
 
 constexpr int DQ_KEYS = 32;  // keys per stage (one step of the contraction)
 
+constexpr int DQ_BUFS = 4;   // stage buffers: the stage computed and three in flight
 template <int D>
 struct DqLds {
-  unsigned char k[2][DQ_KEYS * BCfg<D>::ROWB];  // two stage buffers; K rows stored for transposing reads
-  unsigned char v[2][DQ_KEYS * BCfg<D>::ROWB];  // V rows stored for row reads
+  unsigned char k[DQ_BUFS][DQ_KEYS * BCfg<D>::ROWB];  // K rows stored for transposing reads
+  unsigned char v[DQ_BUFS][DQ_KEYS * BCfg<D>::ROWB];  // V rows stored for row reads
 };
+
+// Wait until at most n (0, 2 or 4) vector-memory instructions of this wave are
+// outstanding, then barrier (no fence: later stages' DMA stays in flight).
+__device__ __forceinline__ void dq_wait_barrier(int n) {
+  if (n >= 4)
+    asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+  else if (n >= 2)
+    asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <int D>
 __global__ __launch_bounds__(512) void dq_kernel(BwdArgs a) {
@@ -128,32 +141,21 @@ __global__ __launch_bounds__(512) void dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) acc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Stage loads: 16-byte chunks, K then V, chunk index cidx = threadIdx.x + 512 u.
-  constexpr int NCH = DQ_KEYS * C::CH;                    // chunks per tile
-  constexpr int PER = (NCH + 511) / 512;                  // per thread per tile
+  // Stage loads: direct global->LDS DMA, one instruction (1 KiB) per wave for K and one
+  // for V. LDS position p of a tile (16-byte units) is key row p / CH, slot p % CH; the
+  // slot holds chunk swz(row, slot) of the row (XOR swizzles are their own inverse).
+  constexpr int NI = DQ_KEYS * C::ROWB / 1024;  // instructions per tile: waves 0..NI-1 issue one each
+  static_assert(NI >= 1 && NI <= DQ_WAVES, "one DMA instruction per issuing wave per tile");
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k) + 2 * (j.kv_tok * a.k_st + int64_t(j.kv) * a.k_sh);
   const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v) + 2 * (j.kv_tok * a.v_st + int64_t(j.kv) * a.v_sh);
-  u32x4 rk[PER], rv[PER];
-  auto load_stage = [&](int st) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int cidx = threadIdx.x + 512 * u;
-      const int key = min(st * DQ_KEYS + cidx / C::CH, j.len - 1);  // past the block: its last key (masked)
-      const int ch = cidx % C::CH;
-      rk[u] = *reinterpret_cast<const u32x4*>(kbase + int64_t(key) * (2 * a.k_st) + 16 * ch);
-      rv[u] = *reinterpret_cast<const u32x4*>(vbase + int64_t(key) * (2 * a.v_st) + 16 * ch);
-    }
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int cidx = threadIdx.x + 512 * u;
-      if (cidx < NCH) {
-        const int row = cidx / C::CH, ch = cidx % C::CH;
-        *reinterpret_cast<u32x4*>(L.k[buf] + row * C::ROWB + 16 * swz_tr<C::CH>(row, ch)) = rk[u];
-        *reinterpret_cast<u32x4*>(L.v[buf] + row * C::ROWB + 16 * swz_row<C::CH>(row, ch)) = rv[u];
-      }
-    }
+  const int srow = (wave * 64 + lane) / C::CH, sslot = (wave * 64 + lane) % C::CH;
+  const int kcc = swz_tr<C::CH>(srow, sslot), vcc = swz_row<C::CH>(srow, sslot);
+  auto issue_stage = [&](int st) {
+    if (wave >= NI) return;
+    const int key = min(st * DQ_KEYS + srow, j.len - 1);  // past the block: its last key (masked)
+    const int buf = st % DQ_BUFS;
+    __builtin_amdgcn_global_load_lds(kbase + int64_t(key) * (2 * a.k_st) + 16 * kcc, (lds_void*)(L.k[buf] + wave * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vbase + int64_t(key) * (2 * a.v_st) + 16 * vcc, (lds_void*)(L.v[buf] + wave * 1024), 16, 0, 0);
   };
   // Per-lane LDS offsets within a 16-row tile: row reads (lane: row li, dims 8G + 32 dc)
   // and K^T reads (lane: dims of tile dt, keys 4G + li/4 and 16 more).
@@ -170,12 +172,12 @@ __global__ __launch_bounds__(512) void dq_kernel(BwdArgs a) {
   }
 
   const int nst = j.nst * (kStageKeys / DQ_KEYS);  // the job's stages of visible keys, in 32-key steps
-  load_stage(0);
+  for (int st = 0; st < DQ_BUFS - 1 && st < nst; ++st) issue_stage(st);
   for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    store_stage(buf);
-    __syncthreads();
-    if (st + 1 < nst) load_stage(st + 1);
+    const int buf = st % DQ_BUFS;
+    // Stage st has landed once only the (at most two) later stages' DMA is pending.
+    dq_wait_barrier(2 * min(DQ_BUFS - 2, nst - 1 - st));
+    if (st + DQ_BUFS - 1 < nst) issue_stage(st + DQ_BUFS - 1);  // into the buffer of stage st - 1
     const unsigned kb = lds_addr(L.k[buf]), vb = lds_addr(L.v[buf]);
     {
       const int key0 = st * DQ_KEYS;  // block key of the stage's first key
@@ -230,7 +232,6 @@ __global__ __launch_bounds__(512) void dq_kernel(BwdArgs a) {
         }
       }
     }
-    __syncthreads();  // every wave is done with this buffer before it is refilled
   }
   // Store the part (lane: row li of the tile, dims 16 dt + 4 G .. + 3).
 #pragma unroll
