@@ -494,6 +494,11 @@ def _bench_backward(skv, M, wl, plan, dev_plan, q, k, v, ws, out, lse, stream, a
     def bstep():
         skv.splitkv_attn_backward(plan, dev_plan, q, k, v, do, out, lse, ws, dq, dk, dv)
 
+    # Untimed calls while the clocks settle (as for the forward), then the warmups.
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_ms * 1e-3:
+        bstep()
+        torch.cuda.synchronize()
     for _ in range(max(1, args.warmup)):
         bstep()
     ms = _time_loop(bstep, max(3, min(args.steps, 10)), stream)
