@@ -1,0 +1,39 @@
+"""The benchmark's JSON line on the GPU: one short in-process run of bench.py's main()."""
+
+import json
+import sys
+
+import pytest
+import torch
+
+from tests.parity import say
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+        "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline")
+
+
+def test_bench_line_contract(capsys, monkeypatch):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bench
+
+    say("[gpu] bench.py main, batch8, 3 steps")
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--workload", "batch8", "--steps", "3", "--warmup", "1",
+                                      "--no-flush", "--settle-ms", "50", "--cpu-budget", "0.5"])
+    assert bench.main() == 0
+    out = capsys.readouterr().out.strip().splitlines()
+    r = json.loads(out[-1])
+    for key in KEYS:
+        assert key in r, key
+    assert r["n_gpus"] == 1 and r["steps"] == 3 and r["warmup"] == 1
+    assert r["config"]["workload"].startswith("batch8") and r["dtype"] == "bf16"
+    assert r["value"] > 0 and r["ms_per_step"] > 0 and r["higher_is_better"] is True
+    ro = r["roofline"]
+    assert ro["bound"] == "hbm" and ro["unit"] == "GB/s" and ro["peak"] == 8000.0
+    assert 0 < ro["frac"] < 1 and abs(ro["frac"] - ro["achieved"] / ro["peak"]) < 1e-3
+    cb = r["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
