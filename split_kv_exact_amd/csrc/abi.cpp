@@ -325,6 +325,7 @@ int splitkv_attn_backward(const splitkv_plan_t* pl, const void* dev_plan, const 
   int64_t tiles = 0;
   for (const splitkv::SeqRec& r : pl->seqs) tiles += (r.n + 63) / 64;
   b.key_tiles = tiles;
+  b.dq_waves = pl->max_rows <= 128 ? 4 : 8;
   return hip_status(splitkv::launch_backward_bf16(b, pl->D, static_cast<hipStream_t>(hip_stream)),
                     "backward launch");
 }

@@ -11,8 +11,9 @@
 // The page describes no kernel; this is a CDNA4 design in four launches:
 //   rowdot:  D_i = <dO_i, O_i> for every query row (one wavefront per row);
 //   dq:      one workgroup per forward job (a unit's KV head and up to 256 of its query
-//            rows): its block's keys stream through LDS in stages of 32 (direct
-//            global->LDS DMA, three stages in flight); each wave keeps
+//            rows; 4 waves when no pass has more than 128 rows, so that two workgroups
+//            share a CU, else 8): its block's keys stream through LDS in stages of 32
+//            (direct global->LDS DMA, three stages in flight); each wave keeps
 //            Q, dO and its dQ part of two 16-row tiles in registers. Scores are computed
 //            transposed as in the forward (S^T = K Q^T), dP^T = V dO^T the same way, and
 //            dQ^T += K^T dS^T with K^T read by transposing LDS loads. The part goes to the
@@ -72,7 +73,6 @@ __global__ __launch_bounds__(256) void rowdot_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dQ parts per job
-constexpr int DQ_WAVES = 8;
 constexpr int RT = 2;  // row tiles per wave
 
 constexpr int DQ_KEYS = 32;  // keys per stage (one step of the contraction)
@@ -84,10 +84,14 @@ struct DqLds {
   unsigned char v[DQ_BUFS][DQ_KEYS * BCfg<D>::ROWB];  // V rows stored for row reads
 };
 
-// Wait until at most n (0, 2 or 4) vector-memory instructions of this wave are
+// Wait until at most n (0, 2, 4, 6 or 8) vector-memory instructions of this wave are
 // outstanding, then barrier (no fence: later stages' DMA stays in flight).
 __device__ __forceinline__ void dq_wait_barrier(int n) {
-  if (n >= 4)
+  if (n >= 8)
+    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  else if (n >= 6)
+    asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+  else if (n >= 4)
     asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
   else if (n >= 2)
     asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
@@ -95,8 +99,8 @@ __device__ __forceinline__ void dq_wait_barrier(int n) {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int D>
-__global__ __launch_bounds__(512) void dq_kernel(BwdArgs a) {
+template <int D, int W>
+__global__ __launch_bounds__(W * 64, 2) void dq_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = BCfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[sizeof(DqLds<D>)];
@@ -107,12 +111,12 @@ __global__ __launch_bounds__(512) void dq_kernel(BwdArgs a) {
   const int G = lane >> 4, li = lane & 15;
   const float c = a.scale * LOG2E;
 
-  // This wave's row tiles: tile_lo + wave and tile_lo + wave + 8.
+  // This wave's row tiles: tile_lo + wave and tile_lo + wave + W.
   int nt = 0;
   int rowq[RT];  // query row of this lane in each tile (rows past the last repeat it)
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
-    const int tile = wave + t * DQ_WAVES;
+    const int tile = wave + t * W;
     if (tile < j.tile_n) nt = t + 1;
     rowq[t] = min((j.tile_lo + min(tile, j.tile_n - 1)) * 16 + li, j.rows - 1);
   }
@@ -141,21 +145,33 @@ __global__ __launch_bounds__(512) void dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) acc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Stage loads: direct global->LDS DMA, one instruction (1 KiB) per wave for K and one
-  // for V. LDS position p of a tile (16-byte units) is key row p / CH, slot p % CH; the
-  // slot holds chunk swz(row, slot) of the row (XOR swizzles are their own inverse).
-  constexpr int NI = DQ_KEYS * C::ROWB / 1024;  // instructions per tile: waves 0..NI-1 issue one each
-  static_assert(NI >= 1 && NI <= DQ_WAVES, "one DMA instruction per issuing wave per tile");
+  // Stage loads: direct global->LDS DMA of 1 KiB per instruction, PW instructions per
+  // issuing wave for K and as many for V. LDS position p of a tile (16-byte units) is key
+  // row p / CH, slot p % CH; the slot holds chunk swz(row, slot) of the row (XOR
+  // swizzles are their own inverse).
+  constexpr int NI = DQ_KEYS * C::ROWB / 1024;  // instructions per tile
+  constexpr int PW = NI > W ? NI / W : 1;        // per issuing wave
+  static_assert(PW * (NI / PW) == NI && NI / PW <= W, "tile split over the waves");
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k) + 2 * (j.kv_tok * a.k_st + int64_t(j.kv) * a.k_sh);
   const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v) + 2 * (j.kv_tok * a.v_st + int64_t(j.kv) * a.v_sh);
-  const int srow = (wave * 64 + lane) / C::CH, sslot = (wave * 64 + lane) % C::CH;
-  const int kcc = swz_tr<C::CH>(srow, sslot), vcc = swz_row<C::CH>(srow, sslot);
+  int srow[PW], kcc[PW], vcc[PW];
+#pragma unroll
+  for (int u = 0; u < PW; ++u) {
+    const int p = (wave * PW + u) * 64 + lane;
+    srow[u] = p / C::CH;
+    kcc[u] = swz_tr<C::CH>(srow[u], p % C::CH);
+    vcc[u] = swz_row<C::CH>(srow[u], p % C::CH);
+  }
   auto issue_stage = [&](int st) {
-    if (wave >= NI) return;
-    const int key = min(st * DQ_KEYS + srow, j.len - 1);  // past the block: its last key (masked)
+    if (wave * PW >= NI) return;
     const int buf = st % DQ_BUFS;
-    __builtin_amdgcn_global_load_lds(kbase + int64_t(key) * (2 * a.k_st) + 16 * kcc, (lds_void*)(L.k[buf] + wave * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vbase + int64_t(key) * (2 * a.v_st) + 16 * vcc, (lds_void*)(L.v[buf] + wave * 1024), 16, 0, 0);
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      const int key = min(st * DQ_KEYS + srow[u], j.len - 1);  // past the block: its last key (masked)
+      const int gi = wave * PW + u;
+      __builtin_amdgcn_global_load_lds(kbase + int64_t(key) * (2 * a.k_st) + 16 * kcc[u], (lds_void*)(L.k[buf] + gi * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vbase + int64_t(key) * (2 * a.v_st) + 16 * vcc[u], (lds_void*)(L.v[buf] + gi * 1024), 16, 0, 0);
+    }
   };
   // Per-lane LDS offsets within a 16-row tile: row reads (lane: row li, dims 8G + 32 dc)
   // and K^T reads (lane: dims of tile dt, keys 4G + li/4 and 16 more).
@@ -176,7 +192,7 @@ __global__ __launch_bounds__(512) void dq_kernel(BwdArgs a) {
   for (int st = 0; st < nst; ++st) {
     const int buf = st % DQ_BUFS;
     // Stage st has landed once only the (at most two) later stages' DMA is pending.
-    dq_wait_barrier(2 * min(DQ_BUFS - 2, nst - 1 - st));
+    dq_wait_barrier(2 * PW * min(DQ_BUFS - 2, nst - 1 - st));
     if (st + DQ_BUFS - 1 < nst) issue_stage(st + DQ_BUFS - 1);  // into the buffer of stage st - 1
     const unsigned kb = lds_addr(L.k[buf]), vb = lds_addr(L.v[buf]);
     {
@@ -499,7 +515,10 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
     if (hipError_t e = hipGetLastError()) return e;
   }
   if (a.num_jobs > 0) {
-    hipLaunchKernelGGL(dq_kernel<D>, dim3(unsigned(a.num_jobs)), dim3(512), 0, stream, a);
+    if (a.dq_waves == 4)
+      hipLaunchKernelGGL((dq_kernel<D, 4>), dim3(unsigned(a.num_jobs)), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((dq_kernel<D, 8>), dim3(unsigned(a.num_jobs)), dim3(512), 0, stream, a);
     if (hipError_t e = hipGetLastError()) return e;
   }
   if (a.total_rows > 0) {

@@ -79,6 +79,7 @@ struct BwdArgs {
   int32_t count;
   int64_t total_rows;
   int64_t key_tiles;  // sum over sequences of ceil(n_s / 64)
+  int32_t dq_waves;   // waves per dQ workgroup: 4 when every pass has at most 8 row tiles, else 8
 };
 
 hipError_t launch_partial_bf16(const PartialArgs& a, int head_dim, hipStream_t stream);
