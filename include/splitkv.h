@@ -52,7 +52,7 @@ extern "C" {
 #endif
 
 #define SPLITKV_VERSION_MAJOR 0
-#define SPLITKV_VERSION_MINOR 5
+#define SPLITKV_VERSION_MINOR 6
 
 typedef enum {
   SPLITKV_OK = 0,
@@ -128,6 +128,20 @@ typedef struct {
   size_t plan_bytes;      /* device plan buffer size for splitkv_plan_upload           */
   size_t workspace_bytes; /* workspace size for partial_attn / merge / attn            */
   size_t ws_lse_offset;   /* byte offset of the partial LSEs inside the workspace      */
+  /* How the bf16 partial-attention launch executes the plan. A job is one unit's KV
+   * head and up to 256 of its query rows; the modelled imbalances below are
+   * (m * max - total) / total over the launch's workgroups:                          */
+  int64_t num_jobs;                 /* jobs of the bf16 kernel                          */
+  double exec_imbalance_static;     /* SPLITKV_SCHED_STATIC lists as run (multi-job units *
+                                     * dealt within XCD classes), under the page's cost   *
+                                     * (a job's pass rows * block length)                 */
+  double exec_imbalance_static_est; /* the same lists under the job-time estimate        *
+                                     * len * max(rows, 128) (see splitkv_schedule)        */
+  double exec_imbalance_queue_est;  /* SPLITKV_SCHED_QUEUE simulated with that estimate: *
+                                     * each workgroup's list without the shared tail,     *
+                                     * then the tail's chunks in order, each to the       *
+                                     * workgroup with the least estimated time so far     */
+  int32_t auto_schedule;            /* what SPLITKV_SCHED_AUTO runs: QUEUE or STATIC     */
 } splitkv_plan_info;
 
 /* Device inputs. Pointers are device memory, caller-owned, read only. Strides are in

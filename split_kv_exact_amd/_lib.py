@@ -76,6 +76,11 @@ class PlanInfo(ctypes.Structure):
         ("plan_bytes", ctypes.c_size_t),
         ("workspace_bytes", ctypes.c_size_t),
         ("ws_lse_offset", ctypes.c_size_t),
+        ("num_jobs", ctypes.c_int64),
+        ("exec_imbalance_static", ctypes.c_double),
+        ("exec_imbalance_static_est", ctypes.c_double),
+        ("exec_imbalance_queue_est", ctypes.c_double),
+        ("auto_schedule", ctypes.c_int32),
     ]
 
 

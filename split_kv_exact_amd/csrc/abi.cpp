@@ -195,6 +195,11 @@ int splitkv_plan_info_get(const splitkv_plan_t* pl, splitkv_plan_info* info) {
   info->plan_bytes = pl->image.size();
   info->workspace_bytes = pl->ws_bytes;
   info->ws_lse_offset = pl->ws_lse_offset;
+  info->num_jobs = pl->num_jobs;
+  info->exec_imbalance_static = pl->exec_static;
+  info->exec_imbalance_static_est = pl->exec_static_est;
+  info->exec_imbalance_queue_est = pl->exec_queue_est;
+  info->auto_schedule = pl->queue_default && pl->tail_start < pl->num_jobs ? SPLITKV_SCHED_QUEUE : SPLITKV_SCHED_STATIC;
   return SPLITKV_OK;
 }
 

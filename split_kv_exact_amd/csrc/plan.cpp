@@ -59,6 +59,21 @@ bool validate_problem(const splitkv_problem* p, std::string* why) {
     total += double(p->kv_lens[s]) * double(std::max<int64_t>(int64_t(p->q_lens[s]) * g, p->cost_ridge_rows)) *
              double(p->num_kv_heads);
   if (total > 4.0e18) return fail("total unit cost beyond 2^62");
+  // Block, unit, job and token indices are int32 in the plan records and the kernels:
+  // the block count of a sequence, the number of units and the number of jobs (a unit
+  // per KV head and pass of up to kPassTiles row tiles) must fit.
+  const int64_t imax = INT32_MAX;
+  int64_t units = 0, jobs = 0;
+  for (int32_t s = 0; s < p->batch; ++s) {
+    const int64_t nb = (p->kv_lens[s] + p->block_len - 1) / p->block_len;
+    if (nb > imax) return fail("a sequence has more than 2^31 - 1 blocks");
+    const int64_t tiles = (int64_t(p->q_lens[s]) * g + 15) / 16;
+    const int64_t passes = (tiles + kPassTiles - 1) / kPassTiles;
+    const int64_t per_block = p->granularity == SPLITKV_UNIT_SEQ_BLOCK_KVHEAD ? p->num_kv_heads : 1;
+    units += nb * per_block;
+    jobs += nb * p->num_kv_heads * passes;
+    if (units > imax || jobs > imax) return fail("more than 2^31 - 1 units or jobs");
+  }
   return true;
 }
 
@@ -364,6 +379,56 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
     if (pl->chunk_ptr.back() != nj) pl->chunk_ptr.push_back(int32_t(nj));
     // Worth its synchronisation only with many jobs per workgroup.
     pl->queue_default = nj >= int64_t(24) * m;
+  }
+  // Modelled balance of the schedules as they execute (the LPT plan's own imbalance is
+  // the assignment of units to workers). A job's share of the page's cost is its pass
+  // rows * len (a unit's jobs add up to its q_s * len * heads).
+  {
+    auto imb = [&](const std::vector<int64_t>& ld) {
+      int64_t tot = 0, mx = 0;
+      for (int64_t x : ld) {
+        tot += x;
+        mx = std::max(mx, x);
+      }
+      return tot == 0 ? 0.0 : double(int64_t(m) * mx - tot) / double(tot);
+    };
+    std::vector<int64_t> pc(nj);
+    for (int64_t i = 0; i < nj; ++i) {
+      const JobRec& j = jobs[i];
+      const int64_t rows = std::min<int64_t>(j.rows, int64_t(j.tile_lo + j.tile_n) * 16) - int64_t(j.tile_lo) * 16;
+      pc[i] = rows * j.len;
+    }
+    // STATIC: workgroup w runs lists_w[w] (after the XCD-class dealing of multi-job units).
+    std::vector<int64_t> lc(m, 0), le(m, 0);
+    for (int32_t w = 0; w < m; ++w)
+      for (int32_t jn : lists_w[w]) {
+        lc[w] += pc[jn];
+        le[w] += jc[jn];
+      }
+    pl->exec_static = imb(lc);
+    pl->exec_static_est = imb(le);
+    // QUEUE: each workgroup's list without the shared tail, then the tail's chunks in
+    // order, each to the workgroup with the least estimated time so far (lowest index on
+    // ties): the run-time rule "next chunk to the first free workgroup" with the
+    // planner's estimate as the time.
+    std::priority_queue<std::pair<int64_t, int32_t>, std::vector<std::pair<int64_t, int32_t>>,
+                        std::greater<std::pair<int64_t, int32_t>>>
+        fr;
+    std::vector<int64_t> lq(m, 0);
+    for (int32_t w = 0; w < m; ++w) {
+      for (int32_t jn : lists_w[w])
+        if (jn < pl->tail_start) lq[w] += jc[jn];
+      fr.emplace(lq[w], w);
+    }
+    for (size_t c = 0; c + 1 < pl->chunk_ptr.size(); ++c) {
+      int64_t t = 0;
+      for (int32_t jn = pl->chunk_ptr[c]; jn < pl->chunk_ptr[c + 1]; ++jn) t += jc[jn];
+      auto e = fr.top();
+      fr.pop();
+      lq[e.second] = e.first + t;
+      fr.emplace(lq[e.second], e.second);
+    }
+    pl->exec_queue_est = imb(lq);
   }
   L.jobs = off;
   off = align16(off + sizeof(JobRec) * jobs.size());

@@ -38,6 +38,10 @@ struct splitkv_plan_s {
   int32_t tail_start = 0;  // queue schedule: first job of the shared tail
   bool queue_default = false;  // SPLITKV_SCHED_AUTO picks the queue
   std::vector<int32_t> chunk_ptr;  // queue schedule: chunk c is jobs [chunk_ptr[c], chunk_ptr[c+1])
+  // Modelled imbalance, (m * max - total) / total over the workgroups, of the schedules
+  // as they run: the static lists under the page's cost and under the job-time
+  // estimate, and the queue schedule simulated with that estimate.
+  double exec_static = 0.0, exec_static_est = 0.0, exec_queue_est = 0.0;
   size_t ws_bytes = 0, ws_lse_offset = 0;
 
   // Device image.

@@ -6,6 +6,9 @@ partial_kernel_bytes: what one launch of the partial-attention kernel must move:
     per unit (sequence s, block b, KV heads), the block's K and V, the unit's query
     rows of Q, and its fp32 partial output and LSE.
 merge_kernel_bytes: partials read once, O and LSE written once.
+partial_traffic_bytes: the fp32 partial outputs and LSEs written by the partial
+    kernel and read back by the merge, 2 * partial_rows * (D + 1) * 4. This is traffic
+    the exact merge costs, never credited as useful bytes.
 flops: 2 flops per multiply-add of QK^T and of PV over the (query, key) pairs the
     mask keeps: 4 * D * Hq * sum_s visible_pairs_s.
 """
@@ -54,6 +57,10 @@ def partial_kernel_bytes(wl) -> int:
     return kv_bytes(wl) + q_per_unit * wl.head_dim * wl.elem_bytes + partial_rows(wl) * (wl.head_dim + 1) * 4
 
 
+def partial_traffic_bytes(wl) -> int:
+    return 2 * partial_rows(wl) * (wl.head_dim + 1) * 4
+
+
 def merge_kernel_bytes(wl) -> int:
     return partial_rows(wl) * (wl.head_dim + 1) * 4 + out_bytes(wl)
 
@@ -61,6 +68,10 @@ def merge_kernel_bytes(wl) -> int:
 def roofline_seconds(wl) -> float:
     peak_f = PEAK_FP32_VECTOR_TFLOPS if wl.dtype == "float32" else PEAK_BF16_MFMA_TFLOPS
     return max(effective_bytes(wl) / (PEAK_HBM_GBS * 1e9), flops(wl) / (peak_f * 1e12))
+
+
+def peak_flops_tflops(wl) -> float:
+    return PEAK_FP32_VECTOR_TFLOPS if wl.dtype == "float32" else PEAK_BF16_MFMA_TFLOPS
 
 
 def binding_roof(wl) -> str:

@@ -78,3 +78,93 @@ def partial_row(wl, s, b, kappa, r):
 
 def scale_of(wl):
     return 1.0 / math.sqrt(wl.head_dim)
+
+
+def oracle_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may use, capped by
+    OMP_NUM_THREADS where the environment sets it (16 on a one-GPU machine)."""
+    import os
+
+    avail = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(avail, int(env))) if env.isdigit() and int(env) > 0 else avail
+
+
+def compare_whole(wl, q, k, v, out, lse, seqs=None, rows_per_task=2048, threads=None, progress=None) -> Diff:
+    """Whole-output parity: the float64 oracle over every (sequence, KV head) of the
+    workload (or of ``seqs``), against the device results ``out`` [sum q, Hq, D] and
+    ``lse`` [sum q, Hq]. Streams one sequence's K/V at a time to the host; the oracle's
+    rows of one KV head are independent, so each (sequence, KV head) is cut into tasks
+    of at most ``rows_per_task`` rows that run on a thread pool (BLAS one thread each).
+    Returns max|dO|, relative L2 over all compared outputs, and max|dLSE|."""
+    import threading
+    from concurrent.futures import ThreadPoolExecutor
+
+    import torch
+
+    from oracle import attend_rows
+
+    threads = threads or oracle_threads()
+    g, d = wl.group, wl.head_dim
+    sc = scale_of(wl)
+    qo, ko = offsets(wl.q_lens), offsets(wl.kv_lens)
+    seqs = range(wl.batch) if seqs is None else seqs
+    o_host = out.detach().cpu().numpy()
+    l_host = lse.detach().cpu().numpy()
+    acc = {"d2": 0.0, "r2": 0.0, "omax": 0.0, "lmax": 0.0, "n": 0}
+    lock = threading.Lock()
+
+    def widen(t):
+        return t.to(torch.float32).numpy().astype(np.float64)
+
+    def task(s, kap, r0, r1, qh, kh, vh):
+        n, qs = wl.kv_lens[s], wl.q_lens[s]
+        Q = widen(qh[:, kap * g:(kap + 1) * g].reshape(qs * g, d)[r0:r1])
+        # K and V come widened when the (sequence, KV head) is split into several tasks.
+        K, V = (kh, vh) if isinstance(kh, np.ndarray) else (widen(kh[:, kap]), widen(vh[:, kap]))
+        pos = np.repeat(np.arange(n - qs, n, dtype=np.int64), g)[r0:r1]
+        O, L = attend_rows(Q, pos, K, V, sc, wl.causal)
+        go = o_host[qo[s]:qo[s + 1], kap * g:(kap + 1) * g].reshape(qs * g, d)[r0:r1].astype(np.float64)
+        gl = l_host[qo[s]:qo[s + 1], kap * g:(kap + 1) * g].reshape(qs * g)[r0:r1].astype(np.float64)
+        assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl)), f"non-finite output in sequence {s}"
+        dd = go - O
+        with lock:
+            acc["d2"] += float(np.sum(dd * dd))
+            acc["r2"] += float(np.sum(O * O))
+            acc["omax"] = max(acc["omax"], float(np.max(np.abs(dd))))
+            acc["lmax"] = max(acc["lmax"], float(np.max(np.abs(gl - L))))
+            acc["n"] += r1 - r0
+
+    try:
+        from threadpoolctl import threadpool_limits
+
+        limiter = threadpool_limits(limits=1, user_api="blas")
+    except Exception:
+        limiter = None
+    try:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            pending = []
+            for s in seqs:
+                qh = q[qo[s]:qo[s + 1]].detach().cpu()
+                kh = k[ko[s]:ko[s + 1]].detach().cpu()
+                vh = v[ko[s]:ko[s + 1]].detach().cpu()
+                rows = wl.q_lens[s] * g
+                for kap in range(wl.num_kv_heads):
+                    kk, vv = (widen(kh[:, kap]), widen(vh[:, kap])) if rows > rows_per_task else (kh, vh)
+                    for r0 in range(0, rows, rows_per_task):
+                        pending.append(ex.submit(task, s, kap, r0, min(rows, r0 + rows_per_task), qh, kk, vv))
+                    del kk, vv
+                # Bound the host copies in flight.
+                while len(pending) > 4 * threads:
+                    pending.pop(0).result()
+                if progress is not None:
+                    progress(s)
+            for f in pending:
+                f.result()
+    finally:
+        if limiter is not None:
+            limiter.unregister()
+    rel = math.sqrt(acc["d2"] / acc["r2"]) if acc["r2"] > 0 else math.sqrt(acc["d2"])
+    res = Diff(acc["omax"], rel, acc["lmax"])
+    res.d2, res.r2 = acc["d2"], acc["r2"]  # sums of squares, to combine parts of one output
+    return res

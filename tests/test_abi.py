@@ -67,6 +67,11 @@ def _problem(kv, q, hq=4, hkv=2, d=128, b=64, m=8, causal=1, gran=0, ridge=0, sp
     dict(kv=[10], q=[2], ridge=(1 << 30) + 1),
     dict(kv=[1 << 40], q=[1 << 20], hq=1024, hkv=1, b=1 << 30),  # total cost beyond 2^62
     dict(kv=[10], q=[2], hq=0),
+    # Block, unit and job indices are int32: 2^40 one-token blocks, or 2^31 units over
+    # two KV heads, are rejected before anything is allocated.
+    dict(kv=[1 << 40], q=[1], hq=1, hkv=1, b=1),
+    dict(kv=[1 << 30], q=[1], hq=2, hkv=2, b=1),
+    dict(kv=[1 << 30], q=[1], hq=2, hkv=2, b=1, gran=1, m=1 << 20),
 ])
 def test_invalid_problems_are_rejected(lib, kw):
     p, keep = _problem(**kw)

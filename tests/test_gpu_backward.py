@@ -104,22 +104,38 @@ def test_backward_is_deterministic():
         assert torch.equal(x, y)
 
 
-@pytest.mark.parametrize("key", ["batch8"])
+def _full_seqs(wl, key):
+    """Sequences whose gradients are sampled: the first and last, and for the mixed
+    workloads decode and prefill ones; for the log-normal mix the shortest and longest
+    contexts and the fewest and most queries."""
+    if key == "mixed":
+        return (0, 127, 128, 131)
+    if key == "lognormal":
+        return tuple(sorted({int(np.argmin(wl.kv_lens)), int(np.argmax(wl.kv_lens)), int(np.argmin(wl.q_lens)),
+                             int(np.argmax(wl.q_lens))}))
+    return tuple(sorted({0, wl.batch - 1}))
+
+
+@pytest.mark.parametrize("key", ["batch8", "long", "lognormal", "decode", "mixed"])
 def test_full_size_backward_sampled(key):
     """Full-size workload in the benchmark's launch configuration, checked on sampled
-    dQ rows and dK / dV keys of two sequences against the oracle at the GPU's forward
-    outputs."""
+    dQ rows and dK / dV keys of several sequences against the oracle at the GPU's
+    forward outputs."""
+    torch.cuda.empty_cache()
     wl = get_workload(key)
     say(f"[gpu] full-size backward {wl.name}")
     q, k, v, do, out, lse, dq, dk, dv = _forward_backward(wl)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert not torch.isnan(t).any(), f"{name} has unwritten entries"
     rng = np.random.default_rng(5)
     qo = np.concatenate([[0], np.cumsum(wl.q_lens)])
     ko = np.concatenate([[0], np.cumsum(wl.kv_lens)])
-    for s in (0, wl.batch - 1):
+    for s in _full_seqs(wl, key):
         n, qs = wl.kv_lens[s], wl.q_lens[s]
-        pairs = sorted({(int(rng.integers(0, qs)), int(rng.integers(0, wl.num_q_heads))) for _ in range(6)})
+        pairs = sorted({(int(rng.integers(0, qs)), int(rng.integers(0, wl.num_q_heads))) for _ in range(6)}
+                       | {(qs - 1, wl.num_q_heads - 1)})
         keys = sorted({(int(rng.integers(0, n)), int(rng.integers(0, wl.num_kv_heads))) for _ in range(6)}
-                      | {(n - 1, 0), (0, wl.num_kv_heads - 1)})
+                      | {(n - 1, 0), (0, wl.num_kv_heads - 1), (n - qs, wl.num_kv_heads // 2)})
         sl, kl = slice(qo[s], qo[s + 1]), slice(ko[s], ko[s + 1])
         rq, rk, rv = grad_sample_ref(widen_to_f64(q[sl]), widen_to_f64(k[kl]), widen_to_f64(v[kl]),
                                      widen_to_f64(do[sl]), widen_to_f64(out[sl]), widen_to_f64(lse[sl]),
@@ -131,3 +147,5 @@ def test_full_size_backward_sampled(key):
             l2, mx = _errors(got, r)
             say(f"    seq {s} {name}: rel L2 {l2:.2e}, max |d| / max |ref| {mx:.2e}")
             assert l2 <= REL_L2 and mx <= REL_MAX, (s, name, l2, mx)
+    del q, k, v, do, out, lse, dq, dk, dv
+    torch.cuda.empty_cache()

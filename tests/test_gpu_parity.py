@@ -1,9 +1,10 @@
 """GPU parity: libsplitkv's HIP kernels against the float64 oracle (needs an MI355X).
 
 Small cases run the whole oracle (every output, every partial). The five workload
-shapes at full size are checked on sampled outputs and sampled partials, in the
-launch configuration the benchmark times (the fused call over the LPT plan).
-Inputs are drawn on the device and copied to the host for the oracle.
+shapes and the decode-only batch at full size are compared whole (every output row),
+with sampled partials, in the launch configuration the benchmark times (the fused
+call over the LPT plan). Inputs are drawn on the device and copied to the host for
+the oracle.
 """
 
 import math
@@ -14,7 +15,7 @@ import torch
 
 import split_kv_exact_amd as skv
 from oracle import attend_rows, attention_ref, partials_ref
-from tests.parity import Diff, assert_within, compare, offsets, partial_row, say, scale_of
+from tests.parity import Diff, assert_within, compare, compare_whole, offsets, partial_row, say, scale_of
 from workloads import Workload, get_workload, make_qkv, widen_to_f64
 
 pytestmark = pytest.mark.gpu
@@ -207,16 +208,23 @@ def test_worker_clock():
 
 
 # --------------------------------------------------------------------------- full sizes
+#
+# Every workload at full size through the fused call over its LPT plan (the launch the
+# benchmark times). Outputs are compared with the float64 oracle over the whole output
+# (streamed per sequence, several host threads); partials are compared on sampled rows
+# of sampled blocks.
 
-def _sample_pairs(rng, wl, s, count):
-    qs = wl.q_lens[s]
-    pairs = {(qs - 1, int(rng.integers(0, wl.num_q_heads))), (0, int(rng.integers(0, wl.num_q_heads)))}
-    while len(pairs) < min(count, qs * wl.num_q_heads):
-        pairs.add((int(rng.integers(0, qs)), int(rng.integers(0, wl.num_q_heads))))
-    return sorted(pairs)
+_FULL = {}
 
 
-def _check_sampled(wl, seqs, per_seq, seed=0, partial_units=4):
+def _full(key):
+    """Inputs, plan and fused outputs of one full-size workload (cached while the next
+    test uses the same workload); the separate calls must give the same bits."""
+    if key in _FULL:
+        return _FULL[key]
+    _FULL.clear()
+    torch.cuda.empty_cache()
+    wl = get_workload(key)
     say(f"[gpu] full-size {wl.name}: drawing inputs")
     q, k, v = make_qkv(wl, "cuda")
     plan = skv.plan_for(wl)
@@ -229,99 +237,136 @@ def _check_sampled(wl, seqs, per_seq, seed=0, partial_units=4):
     torch.cuda.synchronize()
     assert not torch.isnan(out).any() and torch.isfinite(lse).all(), "unwritten or non-finite outputs"
     say(f"[gpu] full-size {wl.name}: separate calls")
-    ws2 = skv.workspace(plan)
-    skv.splitkv_partial_attn(plan, dev_plan, q, k, v, ws2)
-    out2, lse2 = skv.splitkv_merge(plan, dev_plan, ws2)
+    ws.fill_(float("nan"))
+    skv.splitkv_partial_attn(plan, dev_plan, q, k, v, ws)
+    out2, lse2 = skv.splitkv_merge(plan, dev_plan, ws)
     torch.cuda.synchronize()
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
-    wo, wlse = skv.workspace_views(plan, ws2)
+    del out2, lse2
+    _FULL[key] = (wl, q, k, v, plan, ws, out, lse)
+    return _FULL[key]
 
+
+def _whole(key, seqs=None, what=""):
+    wl, q, k, v, plan, ws, out, lse = _full(key)
+    say(f"[gpu] full-size {wl.name}{what}: whole output against the oracle")
+    d = compare_whole(wl, q, k, v, out, lse, seqs=seqs, rows_per_task=1024)
+    say(f"  whole output{what} ({wl.total_q if seqs is None else sum(wl.q_lens[s] for s in seqs)} query tokens "
+        f"x {wl.num_q_heads} heads): {d}")
+    assert_within(d, wl.dtype, f"{wl.name}{what} whole output")
+    return d
+
+
+def _sample_pairs(rng, wl, s, count):
+    qs = wl.q_lens[s]
+    pairs = {(qs - 1, int(rng.integers(0, wl.num_q_heads))), (0, int(rng.integers(0, wl.num_q_heads)))}
+    while len(pairs) < min(count, qs * wl.num_q_heads):
+        pairs.add((int(rng.integers(0, qs)), int(rng.integers(0, wl.num_q_heads))))
+    return sorted(pairs)
+
+
+def _check_partials_sampled(key, seqs, per_seq, seed=0):
+    """Partials of sampled rows (first, last and one middle block of each sampled
+    sequence) against the oracle's per-block attention, read at their ABI rows."""
+    wl, q, k, v, plan, ws, out, lse = _full(key)
+    wo, wlse = skv.workspace_views(plan, ws)
     rng = np.random.default_rng(seed)
     qo, ko = offsets(wl.q_lens), offsets(wl.kv_lens)
     g, sc = wl.group, scale_of(wl)
-    got_o, got_l, ref_o, ref_l = [], [], [], []
     pg_o, pg_l, pr_o, pr_l = [], [], [], []
     for s in seqs:
         n, qs = wl.kv_lens[s], wl.q_lens[s]
-        pairs = _sample_pairs(rng, wl, s, per_seq)
         by_kv = {}
-        for i, h in pairs:
+        for i, h in _sample_pairs(rng, wl, s, per_seq):
             by_kv.setdefault(h // g, []).append((i, h))
         for kap, prs in by_kv.items():
             Kh = widen_to_f64(k[ko[s]:ko[s + 1], kap])
             Vh = widen_to_f64(v[ko[s]:ko[s + 1], kap])
             Qr = np.stack([widen_to_f64(q[qo[s] + i, h]) for i, h in prs])
             pos = np.array([n - qs + i for i, _ in prs], dtype=np.int64)
-            Oref, Lref = attend_rows(Qr, pos, Kh, Vh, sc, wl.causal)
-            for t, (i, h) in enumerate(prs):
-                got_o.append(out[qo[s] + i, h].cpu().numpy())
-                got_l.append(float(lse[qo[s] + i, h]))
-            ref_o.append(Oref)
-            ref_l.append(Lref)
-            # A few partials of the same rows: first block, last block, one in between.
             nb = wl.num_blocks(s)
-            for b in sorted({0, nb - 1, int(rng.integers(0, nb))})[:partial_units]:
+            for b in sorted({0, nb - 1, int(rng.integers(0, nb))}):
                 Ob, Lb = attend_rows(Qr, pos, Kh, Vh, sc, wl.causal, b * wl.block_len, (b + 1) * wl.block_len)
-                for t, (i, h) in enumerate(prs):
+                for i, h in prs:
                     r = partial_row(wl, s, b, kap, i * g + (h - kap * g))
                     pg_o.append(wo[r].cpu().numpy())
                     pg_l.append(float(wlse[r]))
                 pr_o.append(Ob)
                 pr_l.append(Lb)
-    d = compare(np.stack(got_o), np.concatenate(ref_o), np.array(got_l), np.concatenate(ref_l))
     dp = compare(np.stack(pg_o), np.concatenate(pr_o), np.array(pg_l), np.concatenate(pr_l))
-    say(f"  sampled outputs ({len(got_o)}): {d}\n  sampled partials ({len(pg_o)}): {dp}")
-    assert_within(d, wl.dtype, "sampled outputs")
+    say(f"  sampled partials ({len(pg_o)}): {dp}")
     assert_within(dp, wl.dtype, "sampled partials")
-    del q, k, v, ws, ws2
-    torch.cuda.empty_cache()
 
 
 def test_full_small_fp32():
-    wl = get_workload("small")
-    _check_sampled(wl, [0], 4)
-
-
-def test_full_batch8_whole_output():
-    wl = get_workload("batch8")
-    say(f"[gpu] full-size {wl.name}: whole output against the oracle")
-    q, k, v = make_qkv(wl, "cuda")
-    plan = skv.plan_for(wl)
-    dev_plan = skv.splitkv_plan_upload(plan)
-    out, lse = skv.splitkv_attn(plan, dev_plan, q, k, v)
-    torch.cuda.synchronize()
+    wl, q, k, v, plan, ws, out, lse = _full("small")
     O, L = attention_ref(widen_to_f64(q), widen_to_f64(k), widen_to_f64(v), wl.kv_lens, wl.q_lens,
                          wl.num_q_heads, wl.num_kv_heads, wl.causal)
     d = compare(out.cpu().numpy(), O, lse.cpu().numpy(), L)
     say(f"  whole output: {d}")
-    assert_within(d, wl.dtype, "batch8 whole output")
-    _check_sampled(wl, range(8), 6)
+    assert_within(d, wl.dtype, "small fp32 whole output")
+    _check_partials_sampled("small", [0], 4)
 
 
-def test_full_long_context():
-    _check_sampled(get_workload("long"), [0], 24)
+def test_full_batch8_whole_output():
+    _whole("batch8")
+    _check_partials_sampled("batch8", range(8), 6)
 
 
-def test_full_lognormal():
+def test_full_long_whole_output():
+    _whole("long")
+    _check_partials_sampled("long", [0], 24)
+
+
+def test_full_lognormal_whole_output():
     wl = get_workload("lognormal")
+    _whole("lognormal")
     order = np.argsort(wl.kv_lens)
     seqs = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), int(np.argmax(wl.q_lens)),
                    int(np.argmin(wl.q_lens))})
-    _check_sampled(wl, seqs, 8)
+    _check_partials_sampled("lognormal", seqs, 8)
 
 
-def test_full_mixed():
-    wl = get_workload("mixed")
-    _check_sampled(wl, [0, 1, 77, 127, 128, 131], 8)
+def test_full_decode_whole_output():
+    _whole("decode")
+    _check_partials_sampled("decode", [0, 64, 127], 8)
 
 
-def test_full_decode_only():
-    wl = get_workload("decode")
-    _check_sampled(wl, [0, 64, 127], 8)
+# The mixed batch is compared whole in five parts (its 128 decode sequences, then each
+# prefill chunk) so that no single test runs for minutes; the last test combines them.
+_MIXED_PARTS = {}
+
+
+def test_full_mixed_whole_output_decode_part():
+    _MIXED_PARTS["decode"] = _whole("mixed", seqs=range(128), what=" (decode sequences)")
+    _check_partials_sampled("mixed", [0, 1, 77, 127], 8)
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_full_mixed_whole_output_prefill_chunk(chunk):
+    _MIXED_PARTS[f"prefill{chunk}"] = _whole("mixed", seqs=[128 + chunk], what=f" (prefill chunk {chunk})")
+    if chunk in (0, 3):
+        _check_partials_sampled("mixed", [128 + chunk], 8, seed=chunk)
+
+
+def test_full_mixed_whole_output_combined():
+    """Relative L2 over the whole mixed output, from the five parts' sums."""
+    if len(_MIXED_PARTS) < 5:
+        pytest.skip("needs the five parts of the mixed batch in this session")
+    d2 = sum(p.d2 for p in _MIXED_PARTS.values())
+    r2 = sum(p.r2 for p in _MIXED_PARTS.values())
+    d = Diff(max(p.o_max for p in _MIXED_PARTS.values()), math.sqrt(d2 / r2),
+             max(p.lse_max for p in _MIXED_PARTS.values()))
+    say(f"  mixed, whole output: {d}")
+    assert_within(d, "bfloat16", "mixed whole output")
+    _FULL.clear()
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("key", ["batch8", "lognormal", "decode"])
 def test_full_schedules_agree(key):
+    _FULL.clear()
+    torch.cuda.empty_cache()
     wl = get_workload(key)
     say(f"[gpu] full-size {wl.name}: static and queue schedules")
     q, k, v = make_qkv(wl, "cuda")

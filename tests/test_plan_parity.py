@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 
 from oracle import plan_ref
+import split_kv_exact_amd as skv
 from split_kv_exact_amd import splitkv_plan
 from workloads import WORKLOADS, get_workload
 
@@ -72,3 +73,22 @@ def test_xcd_speeds_leave_the_plan_unchanged():
 def skv_plan(wl, speeds):
     from split_kv_exact_amd import plan_for
     return plan_for(wl, 0, speeds).export()
+
+
+def test_executed_schedule_balance():
+    """The plan info's modelled balance of the schedules as they run. When every unit is
+    one job (at most 256 query rows per KV head) the static lists are the plan's worker
+    lists, so under the page's cost their imbalance is the plan's, bit for bit; the
+    job-time estimate and the simulated queue give non-negative figures."""
+    for key in ("batch8", "decode", "lognormal", "mixed", "long"):
+        wl = get_workload(key)
+        inf = skv.plan_for(wl).info()
+        assert inf["num_jobs"] >= inf["num_units"]
+        for f in ("exec_imbalance_static", "exec_imbalance_static_est", "exec_imbalance_queue_est"):
+            assert inf[f] >= 0.0, (key, f)
+        if inf["num_jobs"] == inf["num_units"]:
+            assert inf["exec_imbalance_static"] == inf["imbalance"], key
+        assert inf["auto_schedule"] in (1, 2)
+    # 2048 equal units on 256 workers (two row passes each): every schedule balanced.
+    inf = skv.plan_for(get_workload("long")).info()
+    assert inf["exec_imbalance_static"] == 0.0 and inf["exec_imbalance_queue_est"] == 0.0
