@@ -567,9 +567,9 @@ def milp_makespan(costs, m, time_limit, aggregate=False):
     ``aggregate`` the units of equal cost are one class and the integer variable
     y[c, w] counts the class-c units on worker w (the same optimum: equal-cost units are
     interchangeable), which keeps workload-sized instances to (classes x workers)
-    variables; worker loads are then ordered (load_w >= load_{w+1}), which removes the
-    workers' symmetry without cutting off an optimum. Returns (result, seconds,
-    variables)."""
+    variables. (Ordering the workers' loads to break their symmetry is valid too, but
+    then HiGHS found no feasible point within a minute on the whole workloads.) Returns
+    (result, seconds, variables)."""
     from scipy.optimize import Bounds, LinearConstraint, milp
 
     costs = np.asarray(costs, dtype=np.float64)
@@ -589,12 +589,6 @@ def milp_makespan(costs, m, time_limit, aggregate=False):
         a2[w, w:nc * m:m] = cls
         a2[w, -1] = -1.0
     cons = [LinearConstraint(a1, cnt, cnt), LinearConstraint(a2, -np.inf, 0)]
-    if aggregate and m > 1:
-        a3 = np.zeros((m - 1, nv))
-        for w in range(m - 1):
-            a3[w, w:nc * m:m] = cls
-            a3[w, w + 1:nc * m:m] = -cls
-        cons.append(LinearConstraint(a3, 0, np.inf))
     ub = np.r_[np.repeat(cnt, m), np.inf]
     integ = np.ones(nv)
     integ[-1] = 0
