@@ -235,6 +235,24 @@ int splitkv_merge(const splitkv_plan_t *plan, const void *dev_plan, const float 
 int splitkv_attn(const splitkv_plan_t *plan, void *dev_plan, const splitkv_inputs *in,
                  float *ws, size_t ws_bytes, float *out, float *lse, void *hip_stream);
 
+/* splitkv_attn without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The partials go to a workspace the library holds itself: one array of
+ * SPLITKV_SCRATCH_BYTES (256 MiB) per GPU, in device memory from the library's load
+ * until the process ends. This call allocates nothing (no hipMalloc, no hipFree, no
+ * allocating library routine); the first call on a device looks up that device's
+ * copy of the array. Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (different streams, or different threads without
+ * ordering) race and give wrong results; calls ordered on one stream are safe. Every
+ * workspace row a call reads is written earlier in the same call, so nothing needs
+ * clearing between calls. Same arguments and results as splitkv_attn otherwise.
+ * Errors: as splitkv_attn; WORKSPACE when the plan's workspace_bytes exceeds
+ * SPLITKV_SCRATCH_BYTES (use splitkv_attn with a caller workspace then), reported
+ * before any HIP call; HIP when the array's address cannot be looked up. */
+#define SPLITKV_SCRATCH_BYTES ((size_t)256 << 20)
+int splitkv_attn_scratch(const splitkv_plan_t *plan, void *dev_plan, const splitkv_inputs *in,
+                         float *out, float *lse, void *hip_stream);
+
 /* Inputs of the backward pass besides Q, K and V (device memory, caller-owned). */
 typedef struct {
   const void *d_out;                     /* upstream gradient dO [sum q, Hq, D], the dtype of q */

@@ -12,6 +12,7 @@ from .api import (  # noqa: F401
     plan_for,
     splitkv_attn,
     splitkv_attn_backward,
+    splitkv_attn_scratch,
     splitkv_merge,
     splitkv_partial_attn,
     splitkv_plan,

@@ -25,6 +25,8 @@ SPLITKV_BF16 = 1
 SPLITKV_UNIT_SEQ_BLOCK_KVHEAD = 0
 SPLITKV_UNIT_SEQ_BLOCK = 1
 
+SPLITKV_SCRATCH_BYTES = 256 << 20
+
 SPLITKV_SCHED_AUTO = 0
 SPLITKV_SCHED_QUEUE = 1
 SPLITKV_SCHED_STATIC = 2
@@ -40,6 +42,7 @@ EXPORTED = (
     "splitkv_partial_attn",
     "splitkv_merge",
     "splitkv_attn",
+    "splitkv_attn_scratch",
     "splitkv_attn_backward",
     "splitkv_status_string",
     "splitkv_last_error",
@@ -141,6 +144,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "splitkv_partial_attn": (ctypes.c_int, [P, P, ctypes.POINTER(Inputs), P, ctypes.c_size_t, P]),
         "splitkv_merge": (ctypes.c_int, [P, P, P, ctypes.c_size_t, P, P, P]),
         "splitkv_attn": (ctypes.c_int, [P, P, ctypes.POINTER(Inputs), P, ctypes.c_size_t, P, P, P]),
+        "splitkv_attn_scratch": (ctypes.c_int, [P, P, ctypes.POINTER(Inputs), P, P, P]),
         "splitkv_attn_backward": (ctypes.c_int, [P, P, ctypes.POINTER(Inputs), ctypes.POINTER(Grads), P,
                                                  ctypes.c_size_t, P]),
         "splitkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),

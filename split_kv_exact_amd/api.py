@@ -266,6 +266,21 @@ def splitkv_attn(plan: Plan, dev_plan, q, k, v, ws=None, out=None, lse=None, sca
     return out, lse
 
 
+def splitkv_attn_scratch(plan: Plan, dev_plan, q, k, v, out=None, lse=None, scale: float = 0.0, stream=None,
+                         schedule: str = "auto", clock=None):
+    """Fused partial attention + merge with the library's own device workspace
+    (``splitkv_attn_scratch``): no workspace argument, nothing allocated by the call.
+    Calls that overlap in time on one GPU share that workspace and race."""
+    _check_shapes(plan, q, k, v)
+    out, lse = _outputs(plan, q.device, out, lse)
+    inp = _inputs(q, k, v, scale, schedule, clock)
+    _check(plan._lib, plan._lib.splitkv_attn_scratch(plan.handle, ctypes.c_void_p(dev_plan.data_ptr()),
+                                                     ctypes.byref(inp), ctypes.c_void_p(out.data_ptr()),
+                                                     ctypes.c_void_p(lse.data_ptr()), _stream(stream)),
+           "splitkv_attn_scratch")
+    return out, lse
+
+
 def splitkv_attn_backward(plan: Plan, dev_plan, q, k, v, do, out, lse, ws=None, dq=None, dk=None, dv=None,
                           scale: float = 0.0, stream=None):
     """Gradients dQ, dK, dV (fp32) of sum(do * out) at the forward's ``out`` and ``lse``

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsplitkv.so")
 
-SOURCES = ["abi.cpp", "plan.cpp", "partial_bf16.hip", "partial_f32.hip", "merge.hip", "backward_bf16.hip"]
+SOURCES = ["abi.cpp", "plan.cpp", "partial_bf16.hip", "partial_f32.hip", "merge.hip", "backward_bf16.hip",
+           "scratch.hip"]
 
 ARCH = "gfx950"
 COMMON = [

@@ -273,6 +273,22 @@ int splitkv_attn(const splitkv_plan_t* pl, void* dev_plan, const splitkv_inputs*
   return hip_status(splitkv::launch_merge(m, pl->D, stream), "merge launch");
 }
 
+int splitkv_attn_scratch(const splitkv_plan_t* pl, void* dev_plan, const splitkv_inputs* in, float* out, float* lse,
+                         void* hip_stream) {
+  g_last_error.clear();
+  if (int st = check_plan(pl, dev_plan)) return st;
+  float scale = 0.f;
+  if (int st = check_inputs(pl, in, &scale)) return st;
+  if (int st = check_out(out, lse)) return st;
+  if (pl->ws_bytes > splitkv::kScratchBytes)
+    return fail(SPLITKV_ERR_WORKSPACE, "the plan needs a workspace of " + std::to_string(pl->ws_bytes) +
+                                           " bytes; the library's own holds " +
+                                           std::to_string(splitkv::kScratchBytes) + " (use splitkv_attn)");
+  void* ws = nullptr;
+  if (int st = hip_status(splitkv::scratch_address(&ws), "scratch workspace address")) return st;
+  return splitkv_attn(pl, dev_plan, in, static_cast<float*>(ws), splitkv::kScratchBytes, out, lse, hip_stream);
+}
+
 int splitkv_attn_backward(const splitkv_plan_t* pl, const void* dev_plan, const splitkv_inputs* in,
                           const splitkv_grads* gr, float* ws, size_t ws_bytes, void* hip_stream) {
   g_last_error.clear();

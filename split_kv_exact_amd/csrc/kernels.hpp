@@ -82,6 +82,13 @@ struct BwdArgs {
   int32_t dq_waves;   // waves per dQ workgroup: 4 when every pass has at most 8 row tiles, else 8
 };
 
+// Size of the library's own device workspace (splitkv_attn_scratch), one per GPU.
+constexpr size_t kScratchBytes = size_t(256) << 20;
+
+// Address of the calling thread's current device's copy of that workspace (looked up
+// once per device with hipGetSymbolAddress, then cached).
+hipError_t scratch_address(void** out);
+
 hipError_t launch_partial_bf16(const PartialArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_backward_bf16(const BwdArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_partial_f32(const PartialArgs& a, int head_dim, hipStream_t stream);
