@@ -33,8 +33,8 @@ if ROOT not in sys.path:
 METRIC = "split-KV attention+merge effective HBM GB/s & TFLOP/s, % of MI355X roofline"
 
 
-KERNEL_SOURCES = ("partial_bf16.hip", "partial_f32.hip", "merge.hip", "abi.cpp", "plan.cpp", "kernels.hpp",
-                  "plan_image.hpp", "lds_tiles.hpp")
+KERNEL_SOURCES = ("partial_bf16.hip", "partial_mma.hip", "partial_f32.hip", "merge.hip", "abi.cpp", "plan.cpp",
+                  "kernels.hpp", "plan_image.hpp", "lds_tiles.hpp")
 
 
 def _kernel_sha(csrc: str | None = None) -> str:

@@ -83,9 +83,13 @@ typedef enum { SPLITKV_UNIT_SEQ_BLOCK_KVHEAD = 0, SPLITKV_UNIT_SEQ_BLOCK = 1 } s
  *                        to the first free worker" applied at run time, so workgroups
  *                        that run faster (the CUs differ in memory bandwidth) take
  *                        more of the tail.
- *   SPLITKV_SCHED_AUTO   QUEUE when the plan has at least 24 jobs per workgroup
- *                        (otherwise one chunk is too large a share to balance by),
- *                        else STATIC.
+ *   SPLITKV_SCHED_AUTO   QUEUE when the plan has at least 16 jobs of fewer than 128
+ *                        query rows per workgroup (otherwise one chunk is too large
+ *                        a share to balance by), else STATIC.
+ * Jobs of at least 128 query rows (8 row tiles) run in a launch of their own before
+ * the others, statically: the jobs of each unit go to one XCD's workgroups (which
+ * then share the block through L2) and, within it, each to the workgroup with the
+ * least estimated time; the shared tail holds none of them.
  * All give bitwise identical results (a job's output does not depend on where it
  * runs). fp32 launches always use the static assignment. */
 typedef enum { SPLITKV_SCHED_AUTO = 0, SPLITKV_SCHED_QUEUE = 1, SPLITKV_SCHED_STATIC = 2 } splitkv_schedule;
@@ -142,6 +146,9 @@ typedef struct {
                                      * then the tail's chunks in order, each to the       *
                                      * workgroup with the least estimated time so far     */
   int32_t auto_schedule;            /* what SPLITKV_SCHED_AUTO runs: QUEUE or STATIC     */
+  int64_t num_mma_jobs;             /* jobs of at least 128 query rows (8 row tiles),    *
+                                     * run by a matrix-core kernel in a launch of their  *
+                                     * own before the other jobs' launch                 */
 } splitkv_plan_info;
 
 /* Device inputs. Pointers are device memory, caller-owned, read only. Strides are in

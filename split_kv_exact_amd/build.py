@@ -20,8 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsplitkv.so")
 
-SOURCES = ["abi.cpp", "plan.cpp", "partial_bf16.hip", "partial_f32.hip", "merge.hip", "backward_bf16.hip",
-           "scratch.hip"]
+SOURCES = ["abi.cpp", "plan.cpp", "partial_bf16.hip", "partial_mma.hip", "partial_f32.hip", "merge.hip",
+           "backward_bf16.hip", "scratch.hip"]
 
 ARCH = "gfx950"
 COMMON = [
@@ -40,7 +40,8 @@ COMMON = [
 
 # Per-source extra flags. The bf16 partial kernel produces no NaN from finite inputs
 # (every -inf - -inf is guarded), so its row max needs no NaN quieting.
-EXTRA = {"partial_bf16.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+EXTRA = {"partial_bf16.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+         "partial_mma.hip": ["-fno-honor-nans"]}
 
 
 def _hipcc() -> str:

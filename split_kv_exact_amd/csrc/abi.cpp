@@ -99,6 +99,7 @@ splitkv::PartialArgs partial_args(const splitkv_plan_t* pl, void* dev_plan, cons
   a.jobs = reinterpret_cast<const splitkv::JobRec*>(base + pl->layout.jobs);
   a.wjobs = reinterpret_cast<const int32_t*>(base + pl->layout.wjobs);
   a.job_ptr = reinterpret_cast<const int32_t*>(base + pl->layout.job_ptr);
+  a.split_ptr = reinterpret_cast<const int32_t*>(base + pl->layout.split_ptr);
   a.sched = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(dev_plan) + pl->layout.sched);
   a.chunk_ptr = reinterpret_cast<const int32_t*>(base + pl->layout.chunk_ptr);
   a.num_jobs = int32_t(pl->num_jobs);
@@ -151,10 +152,16 @@ int hip_status(hipError_t e, const char* what) {
   return fail(SPLITKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-int launch_partial(const splitkv_plan_t* pl, const splitkv::PartialArgs& a, int dtype, hipStream_t stream) {
-  hipError_t e = dtype == SPLITKV_BF16 ? splitkv::launch_partial_bf16(a, pl->D, stream)
-                                       : splitkv::launch_partial_f32(a, pl->D, stream);
-  return hip_status(e, "partial attention launch");
+// bf16: the matrix-path jobs (passes of at least 8 row tiles) in one launch, then the
+// other jobs in a second launch on the same stream; each launch only when it has jobs.
+int launch_partial(const splitkv_plan_t* pl, splitkv::PartialArgs a, int dtype, hipStream_t stream) {
+  if (dtype != SPLITKV_BF16) return hip_status(splitkv::launch_partial_f32(a, pl->D, stream), "partial attention launch");
+  const bool mma = pl->num_mma_jobs > 0, rest = pl->num_jobs > pl->num_mma_jobs;
+  if (mma)
+    if (int st = hip_status(splitkv::launch_partial_mma(a, pl->D, stream), "partial attention launch")) return st;
+  a.clock_add = mma ? 1 : 0;
+  if (rest || !mma) return hip_status(splitkv::launch_partial_bf16(a, pl->D, stream), "partial attention launch");
+  return SPLITKV_OK;
 }
 
 }  // namespace
@@ -200,6 +207,7 @@ int splitkv_plan_info_get(const splitkv_plan_t* pl, splitkv_plan_info* info) {
   info->exec_imbalance_static_est = pl->exec_static_est;
   info->exec_imbalance_queue_est = pl->exec_queue_est;
   info->auto_schedule = pl->queue_default && pl->tail_start < pl->num_jobs ? SPLITKV_SCHED_QUEUE : SPLITKV_SCHED_STATIC;
+  info->num_mma_jobs = pl->num_mma_jobs;
   return SPLITKV_OK;
 }
 

@@ -19,7 +19,8 @@ struct PartialArgs {
   const int32_t* worker_ptr;
   const JobRec* jobs;       // bf16 kernel: jobs in LPT order
   const int32_t* wjobs;     // bf16 kernel: job indices of each worker's units
-  const int32_t* job_ptr;   // bf16 kernel: worker w's jobs are wjobs[job_ptr[w] .. job_ptr[w+1])
+  const int32_t* job_ptr;   // bf16 kernels: workgroup w's jobs are wjobs[job_ptr[w] .. job_ptr[w+1]),
+  const int32_t* split_ptr; //   the matrix-path jobs first, up to split_ptr[w]
   uint32_t* sched;          // bf16 kernel: queue counters (next chunk, workgroups done), zero between launches
   const int32_t* chunk_ptr; // bf16 kernel: the shared tail's chunks
   int32_t num_jobs;
@@ -27,6 +28,7 @@ struct PartialArgs {
   int32_t num_chunks;
   int32_t queue;            // bf16 kernel: 1 = shared tail in use
   uint64_t* clock;          // null, or [2 * num_workers] start / end clocks per workgroup
+  int32_t clock_add;        // bf16 kernel: an earlier launch wrote the clocks; add its busy time
   int32_t num_workers;
   int32_t Hq, Hkv, g, B, causal;
   float* ws_o;    // partial outputs [partial_rows, D]
@@ -90,6 +92,7 @@ constexpr size_t kScratchBytes = size_t(256) << 20;
 hipError_t scratch_address(void** out);
 
 hipError_t launch_partial_bf16(const PartialArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_partial_mma(const PartialArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_backward_bf16(const BwdArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_partial_f32(const PartialArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);

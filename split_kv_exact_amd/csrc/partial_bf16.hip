@@ -614,7 +614,7 @@ void partial_bf16_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const i
   lane_offsets<D>(lo, wave, lane, kst, vst);
 
   Feed F;
-  F.sbeg = job_ptr[blockIdx.x];
+  F.sbeg = a.split_ptr[blockIdx.x];  // the jobs before it run in the matrix-path launch
   F.send = job_ptr[blockIdx.x + 1];
   F.cbeg = F.cend = 0;
   F.npop = 0;
@@ -769,7 +769,10 @@ void partial_bf16_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const i
 
   if (threadIdx.x == 0) {
     if (a.clock != nullptr) {
-      a.clock[2 * blockIdx.x] = t_start;
+      // After the matrix-path launch, the start is moved back by that launch's busy time,
+      // so that end - start is the workgroup's busy time in both launches.
+      const uint64_t prev = a.clock_add ? a.clock[2 * blockIdx.x + 1] - a.clock[2 * blockIdx.x] : 0;
+      a.clock[2 * blockIdx.x] = t_start - prev;
       a.clock[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
     }
     if constexpr (queue) {

@@ -287,24 +287,37 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   // its block, one with many by the matrix cores.
   const int64_t nj = int64_t(jobs.size());
   std::vector<int64_t> jc(nj);
-  int64_t jc_total = 0, jc_max = 0;
   for (int64_t i = 0; i < nj; ++i) {
     const JobRec& j = jobs[i];
     const int64_t rows = std::min<int64_t>(j.rows, int64_t(j.tile_lo + j.tile_n) * 16) - int64_t(j.tile_lo) * 16;
     jc[i] = std::max<int64_t>(rows, 128) * j.len;
-    jc_total += jc[i];
-    jc_max = std::max(jc_max, jc[i]);
   }
-  // Execution order of the static lists. Workgroups are spread over the GPU's 8 XCDs
-  // round-robin (workgroup w on XCD w % 8), and the XCDs have their own L2. A unit with
-  // several jobs (row passes, or KV heads of a whole-block unit) reads its block once
-  // per job, so within each XCD class (workers w = x mod 8) the jobs of the multi-job
-  // units assigned to its workers are shared by the class: taken in LPT order, each
-  // goes to the class worker with the least estimated time so far (its own single-job
-  // units counted first), and runs ahead of that worker's single-job units. A unit's
-  // jobs then run at the same time on neighbouring workgroups of one XCD, and the block
-  // is read from HBM about once; the class's workers stay balanced in estimated time.
-  std::vector<std::vector<int32_t>> lists_w(m);
+  // Jobs whose pass covers at least kMmaMinTiles row tiles run in their own launch
+  // (partial_mma.hip); the rest in the launch of partial_bf16.hip. The two launches run
+  // one after the other, so each workgroup's list has a part for each, balanced on its
+  // own.
+  std::vector<char> big(nj, 0);
+  int32_t nbig = 0;
+  for (int64_t i = 0; i < nj; ++i) {
+    big[i] = jobs[i].tile_n >= kMmaMinTiles;
+    nbig += big[i];
+  }
+  auto unit_big = [&](int64_t u) {
+    int32_t c = 0;
+    for (int32_t k = 0; k < unit_njob[u]; ++k) c += big[unit_job[u] + k];
+    return c;
+  };
+  // Execution order of the lists of the other launch. Workgroups are spread over the
+  // GPU's 8 XCDs round-robin (workgroup w on XCD w % 8), and the XCDs have their own L2.
+  // A unit with several jobs (row passes, or KV heads of a whole-block unit) reads its
+  // block once per job, so within each XCD class (workers w = x mod 8) the jobs of the
+  // multi-job units assigned to its workers are shared by the class: taken in LPT
+  // order, each goes to the class worker with the least estimated time so far (its own
+  // single-job units counted first), and runs ahead of that worker's single-job units. A
+  // unit's jobs then run at the same time on neighbouring workgroups of one XCD, and the
+  // block is read from HBM about once; the class's workers stay balanced in estimated
+  // time.
+  std::vector<std::vector<int32_t>> lists_w(m), lists_big(m);
   const int32_t ncls = (m % 8 == 0 && m >= 16) ? 8 : 1;
   // A block read by one job, or by jobs dealt to distinct workers of one class (which
   // read it at about the same time), is not read again afterwards: its K/V loads carry
@@ -312,17 +325,19 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   for (int64_t u = 0; u < n; ++u)
     if (unit_njob[u] == 1 || (ncls > 1 && unit_njob[u] <= m / ncls))
       for (int32_t k = 0; k < unit_njob[u]; ++k) jobs[unit_job[u] + k].flags |= kJobStream;
+  typedef std::pair<int64_t, int32_t> LoadW;  // (estimated time, slot or class)
   for (int32_t x = 0; x < ncls; ++x) {
     std::vector<int32_t> shared;
-    typedef std::pair<int64_t, int32_t> LoadW;  // (estimated time, slot)
     std::priority_queue<LoadW, std::vector<LoadW>, std::greater<LoadW>> heap;
     for (int32_t sl = x; sl < m; sl += ncls) {
       const int32_t w = pl->slot_worker[sl];
       int64_t own = 0;
       for (int32_t i = pl->worker_ptr[w]; i < pl->worker_ptr[w + 1]; ++i) {
         const int32_t u = pl->worker_units[i];
+        const bool multi = unit_njob[u] - unit_big(u) > 1 && ncls > 1;
         for (int32_t k = 0; k < unit_njob[u]; ++k) {
-          if (unit_njob[u] > 1 && ncls > 1)
+          if (big[unit_job[u] + k]) continue;
+          if (multi)
             shared.push_back(unit_job[u] + k);
           else
             own += jc[unit_job[u] + k];
@@ -342,18 +357,72 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
       const int32_t w = pl->slot_worker[sl];
       for (int32_t i = pl->worker_ptr[w]; i < pl->worker_ptr[w + 1]; ++i) {
         const int32_t u = pl->worker_units[i];
-        if (unit_njob[u] == 1 || ncls == 1)
-          for (int32_t k = 0; k < unit_njob[u]; ++k) lists_w[sl].push_back(unit_job[u] + k);
+        if (unit_njob[u] - unit_big(u) == 1 || ncls == 1)
+          for (int32_t k = 0; k < unit_njob[u]; ++k)
+            if (!big[unit_job[u] + k]) lists_w[sl].push_back(unit_job[u] + k);
       }
     }
   }
+  // The matrix-path launch: the units' jobs in LPT order (unit cost descending), each
+  // unit's jobs to the XCD class with the least estimated time so far (its passes then
+  // share one L2), and within the class each job to the workgroup with the least
+  // estimated time so far (ties to the lowest index).
+  {
+    std::vector<std::vector<int32_t>> cls_jobs(ncls);
+    std::priority_queue<LoadW, std::vector<LoadW>, std::greater<LoadW>> ch;
+    for (int32_t x = 0; x < ncls; ++x) ch.push(LoadW(0, x));
+    for (int64_t i = 0; i < n; ++i) {
+      const int32_t u = order[i];
+      if (unit_big(u) == 0) continue;
+      LoadW e = ch.top();
+      ch.pop();
+      for (int32_t k = 0; k < unit_njob[u]; ++k)
+        if (big[unit_job[u] + k]) {
+          cls_jobs[e.second].push_back(unit_job[u] + k);
+          e.first += jc[unit_job[u] + k];
+        }
+      ch.push(e);
+    }
+    for (int32_t x = 0; x < ncls; ++x) {
+      std::priority_queue<LoadW, std::vector<LoadW>, std::greater<LoadW>> heap;
+      for (int32_t sl = x; sl < m; sl += ncls) heap.push(LoadW(0, sl));
+      for (int32_t jn : cls_jobs[x]) {
+        LoadW e = heap.top();
+        heap.pop();
+        lists_big[e.second].push_back(jn);
+        e.first += jc[jn];
+        heap.push(e);
+      }
+    }
+  }
+  // Job numbers: the matrix-path jobs first, then the others, each group in LPT order.
+  std::vector<int32_t> perm(nj);
+  {
+    int32_t a = 0, b = nbig;
+    for (int64_t i = 0; i < nj; ++i) perm[i] = big[i] ? a++ : b++;
+    std::vector<JobRec> jobs2(nj);
+    std::vector<int64_t> jc2(nj);
+    for (int64_t i = 0; i < nj; ++i) {
+      jobs2[perm[i]] = jobs[i];
+      jc2[perm[i]] = jc[i];
+    }
+    jobs.swap(jobs2);
+    jc.swap(jc2);
+  }
   std::vector<int32_t> wjobs;
   wjobs.reserve(jobs.size());
-  std::vector<int32_t> job_ptr(m + 1, 0);
+  std::vector<int32_t> job_ptr(m + 1, 0), split_ptr(m, 0);
   for (int32_t w = 0; w < m; ++w) {
-    wjobs.insert(wjobs.end(), lists_w[w].begin(), lists_w[w].end());
+    for (int32_t jn : lists_big[w]) wjobs.push_back(perm[jn]);
+    split_ptr[w] = int32_t(wjobs.size());
+    for (int32_t jn : lists_w[w]) wjobs.push_back(perm[jn]);
     job_ptr[w + 1] = int32_t(wjobs.size());
   }
+  for (int32_t w = 0; w < m; ++w) {
+    lists_big[w].assign(wjobs.begin() + job_ptr[w], wjobs.begin() + split_ptr[w]);
+    lists_w[w].assign(wjobs.begin() + split_ptr[w], wjobs.begin() + job_ptr[w + 1]);
+  }
+  pl->num_mma_jobs = nbig;
   pl->num_jobs = int64_t(jobs.size());
   // Queue schedule. The jobs at the end of the LPT order that make up the last fifth
   // of the estimated time form the shared tail, cut into chunks of consecutive jobs of
@@ -362,9 +431,14 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   // sub-queue w % kQueues (workgroups are spread over the XCDs round-robin, so each
   // sub-queue has one XCD's workgroups as first takers).
   {
-    const int64_t total = jc_total, maxc = jc_max;
+    // Only jobs of the partial_bf16 launch (numbered from nbig on) take part.
+    int64_t total = 0, maxc = 0;
+    for (int64_t i = nbig; i < nj; ++i) {
+      total += jc[i];
+      maxc = std::max(maxc, jc[i]);
+    }
     int64_t h = nj, acc = 0;
-    while (h > 0 && acc * 5 < total) acc += jc[--h];
+    while (h > nbig && acc * 5 < total) acc += jc[--h];
     pl->tail_start = int32_t(h);
     const int64_t target = std::max<int64_t>(1, std::min(maxc / 2, total / (int64_t(m) * 32)));
     pl->chunk_ptr.assign(1, int32_t(h));
@@ -378,19 +452,22 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
     }
     if (pl->chunk_ptr.back() != nj) pl->chunk_ptr.push_back(int32_t(nj));
     // Worth its synchronisation only with many jobs per workgroup.
-    pl->queue_default = nj >= int64_t(24) * m;
+    pl->queue_default = nj - nbig >= int64_t(16) * m;
   }
   // Modelled balance of the schedules as they execute (the LPT plan's own imbalance is
   // the assignment of units to workers). A job's share of the page's cost is its pass
-  // rows * len (a unit's jobs add up to its q_s * len * heads).
+  // rows * len (a unit's jobs add up to its q_s * len * heads). The two launches run one
+  // after the other, so the modelled time is the sum of their largest workgroup loads:
+  // imbalance = (m * (max_w big_w + max_w other_w) - total) / total.
   {
-    auto imb = [&](const std::vector<int64_t>& ld) {
-      int64_t tot = 0, mx = 0;
-      for (int64_t x : ld) {
-        tot += x;
-        mx = std::max(mx, x);
+    auto imb = [&](const std::vector<int64_t>& a, const std::vector<int64_t>& b) {
+      int64_t tot = 0, ma = 0, mb = 0;
+      for (int32_t w = 0; w < m; ++w) {
+        tot += a[w] + b[w];
+        ma = std::max(ma, a[w]);
+        mb = std::max(mb, b[w]);
       }
-      return tot == 0 ? 0.0 : double(int64_t(m) * mx - tot) / double(tot);
+      return tot == 0 ? 0.0 : double(int64_t(m) * (ma + mb) - tot) / double(tot);
     };
     std::vector<int64_t> pc(nj);
     for (int64_t i = 0; i < nj; ++i) {
@@ -398,15 +475,19 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
       const int64_t rows = std::min<int64_t>(j.rows, int64_t(j.tile_lo + j.tile_n) * 16) - int64_t(j.tile_lo) * 16;
       pc[i] = rows * j.len;
     }
-    // STATIC: workgroup w runs lists_w[w] (after the XCD-class dealing of multi-job units).
-    std::vector<int64_t> lc(m, 0), le(m, 0);
-    for (int32_t w = 0; w < m; ++w)
+    std::vector<int64_t> bc(m, 0), be(m, 0), lc(m, 0), le(m, 0);
+    for (int32_t w = 0; w < m; ++w) {
+      for (int32_t jn : lists_big[w]) {
+        bc[w] += pc[jn];
+        be[w] += jc[jn];
+      }
       for (int32_t jn : lists_w[w]) {
         lc[w] += pc[jn];
         le[w] += jc[jn];
       }
-    pl->exec_static = imb(lc);
-    pl->exec_static_est = imb(le);
+    }
+    pl->exec_static = imb(bc, lc);
+    pl->exec_static_est = imb(be, le);
     // QUEUE: each workgroup's list without the shared tail, then the tail's chunks in
     // order, each to the workgroup with the least estimated time so far (lowest index on
     // ties): the run-time rule "next chunk to the first free workgroup" with the
@@ -428,7 +509,7 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
       lq[e.second] = e.first + t;
       fr.emplace(lq[e.second], e.second);
     }
-    pl->exec_queue_est = imb(lq);
+    pl->exec_queue_est = imb(be, lq);
   }
   L.jobs = off;
   off = align16(off + sizeof(JobRec) * jobs.size());
@@ -436,6 +517,8 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   off = align16(off + sizeof(int32_t) * std::max<size_t>(wjobs.size(), 1));
   L.job_ptr = off;
   off = align16(off + sizeof(int32_t) * uint64_t(m + 1));
+  L.split_ptr = off;
+  off = align16(off + sizeof(int32_t) * uint64_t(m));
   L.chunk_ptr = off;
   off = align16(off + sizeof(int32_t) * pl->chunk_ptr.size());
   off = (off + 255) & ~uint64_t(255);
@@ -480,6 +563,7 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   if (!jobs.empty()) std::memcpy(base + L.jobs, jobs.data(), sizeof(JobRec) * jobs.size());
   if (!wjobs.empty()) std::memcpy(base + L.wjobs, wjobs.data(), sizeof(int32_t) * wjobs.size());
   std::memcpy(base + L.job_ptr, job_ptr.data(), sizeof(int32_t) * (m + 1));
+  std::memcpy(base + L.split_ptr, split_ptr.data(), sizeof(int32_t) * m);
   std::memcpy(base + L.chunk_ptr, pl->chunk_ptr.data(), sizeof(int32_t) * pl->chunk_ptr.size());
   // The scheduling area (L.sched) stays zero: launches leave it that way.
 }

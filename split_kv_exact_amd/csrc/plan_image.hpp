@@ -37,6 +37,8 @@ constexpr int32_t kStageKeys = 64;
 constexpr int32_t kQTileRows = 64;
 // Row tiles of 16 query rows that one pass of the bf16 kernel covers.
 constexpr int32_t kPassTiles = 16;
+// Passes of at least this many row tiles run on the matrix path (partial_mma.hip).
+constexpr int32_t kMmaMinTiles = 8;
 
 // The plan's scheduling area: kQueues uint32 counters of the shared tail's
 // sub-queues (the next entry of each; one per 64-byte line, so that workgroups on
@@ -82,6 +84,7 @@ struct ImageLayout {
   uint64_t jobs;        // JobRec[num_jobs] in LPT order
   uint64_t wjobs;       // int32[num_jobs]: job indices of each workgroup's units, workgroup by workgroup
   uint64_t job_ptr;     // int32[m + 1]: workgroup w's jobs are wjobs[job_ptr[w] .. job_ptr[w+1])
+  uint64_t split_ptr;   // int32[m]: of those, the matrix-path jobs come first, up to split_ptr[w]
   uint64_t chunk_ptr;   // int32[num_chunks + 1]: the shared tail's chunks of consecutive jobs
   uint64_t sched;       // kSchedBytes, 256-byte aligned: counters of the shared job queue
   uint64_t total;

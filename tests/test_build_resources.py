@@ -46,7 +46,8 @@ def _resources(src):
     return kernels
 
 
-@pytest.mark.parametrize("src", ["partial_bf16.hip", "partial_f32.hip", "merge.hip", "backward_bf16.hip"])
+@pytest.mark.parametrize("src", ["partial_bf16.hip", "partial_mma.hip", "partial_f32.hip", "merge.hip",
+                                 "backward_bf16.hip"])
 def test_no_scratch_and_no_spills(src):
     ks = _resources(src)
     assert ks, "no kernels reported"
@@ -55,7 +56,8 @@ def test_no_scratch_and_no_spills(src):
         assert res.get("VGPRs Spill", 0) == 0, (name, res)
 
 
-def test_partial_bf16_fits_two_waves_per_simd():
-    for name, res in _resources("partial_bf16.hip").items():
+@pytest.mark.parametrize("src", ["partial_bf16.hip", "partial_mma.hip"])
+def test_partial_kernels_fit_two_waves_per_simd(src):
+    for name, res in _resources(src).items():
         assert res.get("VGPRs", 999) + res.get("AGPRs", 0) <= 256, (name, res)
         assert res.get("Occupancy", 2) >= 2, (name, res)
