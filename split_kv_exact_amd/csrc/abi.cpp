@@ -158,7 +158,9 @@ int launch_partial(const splitkv_plan_t* pl, splitkv::PartialArgs a, int dtype, 
   if (dtype != SPLITKV_BF16) return hip_status(splitkv::launch_partial_f32(a, pl->D, stream), "partial attention launch");
   const bool mma = pl->num_mma_jobs > 0, rest = pl->num_jobs > pl->num_mma_jobs;
   if (mma)
-    if (int st = hip_status(splitkv::launch_partial_mma(a, pl->D, stream), "partial attention launch")) return st;
+    if (int st = hip_status(splitkv::launch_partial_mma(a, pl->D, pl->mma_partial_passes, stream),
+                            "partial attention launch"))
+      return st;
   a.clock_add = mma ? 1 : 0;
   if (rest || !mma) return hip_status(splitkv::launch_partial_bf16(a, pl->D, stream), "partial attention launch");
   return SPLITKV_OK;

@@ -92,7 +92,8 @@ constexpr size_t kScratchBytes = size_t(256) << 20;
 hipError_t scratch_address(void** out);
 
 hipError_t launch_partial_bf16(const PartialArgs& a, int head_dim, hipStream_t stream);
-hipError_t launch_partial_mma(const PartialArgs& a, int head_dim, hipStream_t stream);
+// partial_passes: some matrix-path pass has fewer than 16 row tiles.
+hipError_t launch_partial_mma(const PartialArgs& a, int head_dim, bool partial_passes, hipStream_t stream);
 hipError_t launch_backward_bf16(const BwdArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_partial_f32(const PartialArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);

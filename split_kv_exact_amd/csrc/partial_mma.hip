@@ -11,7 +11,8 @@
 // Execution model
 //   * One workgroup of 8 wavefronts (two per SIMD) per workgroup slot of the plan; it
 //     walks its list of jobs, each cut into stages of 64 keys. Every wave computes: wave
-//     w owns row tiles w and w + 8 of the pass (16 rows each; rows past the job's last
+//     w owns row tiles w and w + 8 of the pass (16 rows each; a pass has 8 to 16 tiles,
+//     and a wave whose second tile lies past the pass skips it; rows past the job's last
 //     row repeat it and are stored as duplicates of identical values).
 //   * Four LDS slots hold stages (a K tile and a V tile each, XOR-swizzled exactly as in
 //     the other kernel). Every wave issues one eighth of each stage by direct global->LDS
@@ -237,25 +238,33 @@ __device__ __forceinline__ void k_read(bf16x8 (&k)[2][Cfg<D>::DC], const unsigne
 
 // S^T = K Q^T for the step: s[t][tt] holds row tile t against key tile tt.
 template <int D>
-__device__ __forceinline__ void scores(f32x4 (&s)[2][2], const State<D>& st, const bf16x8 (&k)[2][Cfg<D>::DC]) {
+__device__ __forceinline__ void scores_tile(f32x4 (&s)[2][2], const State<D>& st, const bf16x8 (&k)[2][Cfg<D>::DC],
+                                            int t) {
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+  for (int tt = 0; tt < 2; ++tt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int dc = 0; dc < Cfg<D>::DC; ++dc) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[tt][dc], st.q[t][dc], acc, 0, 0, 0);
-      s[t][tt] = acc;
-    }
+    for (int dc = 0; dc < Cfg<D>::DC; ++dc) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[tt][dc], st.q[t][dc], acc, 0, 0, 0);
+    s[t][tt] = acc;
+  }
+}
+// two: the wave's second row tile lies inside the pass (wave-uniform); otherwise its
+// work is skipped.
+template <int D>
+__device__ __forceinline__ void scores(f32x4 (&s)[2][2], const State<D>& st, const bf16x8 (&k)[2][Cfg<D>::DC],
+                                       bool two) {
+  scores_tile<D>(s, st, k, 0);
+  if (two) scores_tile<D>(s, st, k, 1);
 }
 
 // Mask, reference max, p = 2^(s*c - m*c): rounded to bf16 into p, fp32 sum into l.
 template <int D>
 __device__ __forceinline__ void softmax(f32x4 (&s)[2][2], State<D>& st, bf16x4 (&p)[2][2], int key0, bool mask,
-                                        float c, float inv_c) {
+                                        bool two, float c, float inv_c) {
   const int G = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
+    if (t == 1 && !two) break;
     if (mask) {
       // Entry e of key tile tt is step key key0 + 16tt + 4G + e.
       const int d = st.lim[t] - (key0 + 4 * G);
@@ -295,11 +304,12 @@ __device__ __forceinline__ void softmax(f32x4 (&s)[2][2], State<D>& st, bf16x4 (
 // O^T += V^T P^T for both row tiles, and the rounded p summed on the matrix core.
 template <int D>
 __device__ __forceinline__ void pv(State<D>& st, const bf16x4 (&p)[2][2], const i16x4 (&vlo)[Cfg<D>::DT],
-                                   const i16x4 (&vhi)[Cfg<D>::DT]) {
+                                   const i16x4 (&vhi)[Cfg<D>::DT], bool two) {
   const __bf16 one = (__bf16)1.0f;
   const bf16x8 ones = {one, one, one, one, one, one, one, one};
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
+    if (t == 1 && !two) break;
     const bf16x8 pb = __builtin_shufflevector(p[t][0], p[t][1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
     for (int dt = 0; dt < Cfg<D>::DT; ++dt) {
@@ -315,7 +325,8 @@ __device__ __forceinline__ void pv(State<D>& st, const bf16x4 (&p)[2][2], const 
 // requested before the call.
 template <int D>
 __device__ __forceinline__ void stage(State<D>& st, bf16x8 (&kA)[2][Cfg<D>::DC], const unsigned (&ka)[Cfg<D>::DC],
-                                      const unsigned (&va)[Cfg<D>::DT], int key0, bool mask, float c, float inv_c) {
+                                      const unsigned (&va)[Cfg<D>::DT], int key0, bool mask, bool two, float c,
+                                      float inv_c) {
   using C = Cfg<D>;
   f32x4 s[2][2];
   bf16x4 p[2][2];
@@ -323,18 +334,18 @@ __device__ __forceinline__ void stage(State<D>& st, bf16x8 (&kA)[2][Cfg<D>::DC],
   bf16x8 kB[2][C::DC];
   // Step A: scores; this step's V^T requested under the softmax, the next step's K
   // under the P V products.
-  scores<D>(s, st, kA);
+  scores<D>(s, st, kA, two);
   vt_issue<0, 16 * C::ROWB>(vlo, vhi, va);
-  softmax<D>(s, st, p, key0, mask, c, inv_c);
+  softmax<D>(s, st, p, key0, mask, two, c, inv_c);
   vt_wait(vlo, vhi);
   k_read<D, 32 * C::ROWB>(kB, ka);
-  pv<D>(st, p, vlo, vhi);
+  pv<D>(st, p, vlo, vhi, two);
   // Step B.
-  scores<D>(s, st, kB);
+  scores<D>(s, st, kB, two);
   vt_issue<32 * C::ROWB, 16 * C::ROWB>(vlo, vhi, va);
-  softmax<D>(s, st, p, key0 + 32, mask, c, inv_c);
+  softmax<D>(s, st, p, key0 + 32, mask, two, c, inv_c);
   vt_wait(vlo, vhi);
-  pv<D>(st, p, vlo, vhi);
+  pv<D>(st, p, vlo, vhi, two);
 }
 
 // Query row of tile `tile`, lane row li; rows past the last one repeat it.
@@ -372,7 +383,9 @@ __device__ __forceinline__ void write_tile(const State<D>& st, int t, const Part
   __builtin_nontemporal_store(lse, lp);
 }
 
-template <int D>
+// PARTIAL: the launch has passes of fewer than 16 row tiles, whose waves skip a second
+// tile past the pass; without it every wave always computes two tiles (no branches).
+template <int D, bool PARTIAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void partial_mma_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const int32_t* __restrict__ wjobs,
                         const int32_t* __restrict__ job_ptr, const int32_t* __restrict__ split_ptr) {
@@ -455,6 +468,7 @@ void partial_mma_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const in
   int jj = 0;    // its stage
   int nst = 0, len = 0;
   int min_lim = 0, max_lim = 0;
+  bool two = true;
   for (int s = 0; s < issued; ++s) {
     // Stage s has landed for this wave once only the instructions issued after it are
     // pending; the barrier makes every wave's part visible and frees slot (s - 1) % NST.
@@ -483,6 +497,7 @@ void partial_mma_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const in
         for (int dc = 0; dc < C::DC; ++dc)
           st.q[t][dc] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * dc));
       }
+      two = !PARTIAL || wave + 8 < j.tile_n;
       const int r_first = tile_row(j, j.tile_lo + wave, 0);
       const int r_last = tile_row(j, j.tile_lo + wave + 8, 15);
       min_lim = min(j.lim0 + r_first / a.g, j.len - 1);
@@ -503,15 +518,15 @@ void partial_mma_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const in
       for (int dt = 0; dt < C::DT; ++dt) va[dt] = sb + C::TILEB + lo.vr[dt];
       bf16x8 kA[2][C::DC];
       k_read<D, 0>(kA, ka);
-      stage<D>(st, kA, ka, va, key0, key0 + TK - 1 > min_lim, c, inv_c);
+      stage<D>(st, kA, ka, va, key0, key0 + TK - 1 > min_lim, two, c, inv_c);
     }
     if (issue()) cnt[AHEAD - 1] = 0;
     if (++jj == nst) {
       const JobRec j = jobs[wjobs[ci]];
+      write_tile<D>(st, 0, a, j, j.tile_lo + wave);
+      if (two) write_tile<D>(st, 1, a, j, j.tile_lo + wave + 8);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) write_tile<D>(st, t, a, j, j.tile_lo + wave + 8 * t);
-#pragma unroll
-      for (int x = 0; x <= AHEAD; ++x) cnt[x] += 2 * C::STORES;
+      for (int x = 0; x <= AHEAD; ++x) cnt[x] += (two ? 2 : 1) * C::STORES;
       reset<D>(st);
       ++ci;
       jj = 0;
@@ -527,14 +542,24 @@ void partial_mma_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const in
 
 }  // namespace
 
-hipError_t launch_partial_mma(const PartialArgs& a, int head_dim, hipStream_t stream) {
+hipError_t launch_partial_mma(const PartialArgs& a, int head_dim, bool partial_passes, hipStream_t stream) {
   const dim3 grid(a.num_workers), block(NW * 64);
-  if (head_dim == 128)
-    hipLaunchKernelGGL((partial_mma_kernel<128>), grid, block, 0, stream, a, a.jobs, a.wjobs, a.job_ptr, a.split_ptr);
-  else if (head_dim == 64)
-    hipLaunchKernelGGL((partial_mma_kernel<64>), grid, block, 0, stream, a, a.jobs, a.wjobs, a.job_ptr, a.split_ptr);
-  else
+#define SKV_LAUNCH(DD, P) \
+  hipLaunchKernelGGL((partial_mma_kernel<DD, P>), grid, block, 0, stream, a, a.jobs, a.wjobs, a.job_ptr, a.split_ptr)
+  if (head_dim == 128) {
+    if (partial_passes)
+      SKV_LAUNCH(128, true);
+    else
+      SKV_LAUNCH(128, false);
+  } else if (head_dim == 64) {
+    if (partial_passes)
+      SKV_LAUNCH(64, true);
+    else
+      SKV_LAUNCH(64, false);
+  } else {
     return hipErrorInvalidValue;
+  }
+#undef SKV_LAUNCH
   return hipGetLastError();
 }
 

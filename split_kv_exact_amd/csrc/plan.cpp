@@ -261,8 +261,12 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
     const int32_t lim0 = pl->causal ? int32_t(std::min<int64_t>(len, r.n - r.q - key0)) : len;
     const int32_t nrt = (r.rows + 15) / 16;
     const int32_t kv_lo = per_head ? pl->u_kv[u] : 0, kv_hi = per_head ? kv_lo + 1 : Hkv;
+    // Row passes of at most kPassTiles tiles, as even as possible (a unit's passes are
+    // then alike, and run in the same launch).
+    const int32_t npass = (nrt + kPassTiles - 1) / kPassTiles;
     for (int32_t kv = kv_lo; kv < kv_hi; ++kv) {
-      for (int32_t t0 = 0; t0 < nrt; t0 += kPassTiles) {
+      for (int32_t pi = 0, t0 = 0; pi < npass; ++pi) {
+        const int32_t tn = nrt / npass + (pi < nrt % npass ? 1 : 0);
         JobRec j{};
         j.kv_tok = r.kv_base + key0;
         j.q_tok = r.q_base;
@@ -272,7 +276,8 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
         j.lim0 = lim0;
         j.rows = r.rows;
         j.tile_lo = t0;
-        j.tile_n = std::min(kPassTiles, nrt - t0);
+        j.tile_n = tn;
+        t0 += tn;
         const int32_t rmax = std::min(r.rows, (t0 + j.tile_n) * 16) - 1;
         const int64_t tmax = std::min<int64_t>(len - 1, int64_t(lim0) + rmax / g);
         j.nst = tmax < 0 ? 1 : int32_t(tmax / kStageKeys) + 1;
@@ -423,6 +428,9 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
     lists_w[w].assign(wjobs.begin() + split_ptr[w], wjobs.begin() + job_ptr[w + 1]);
   }
   pl->num_mma_jobs = nbig;
+  pl->mma_partial_passes = false;
+  for (int32_t i = 0; i < nbig; ++i)
+    if (jobs[i].tile_n < kPassTiles) pl->mma_partial_passes = true;
   pl->num_jobs = int64_t(jobs.size());
   // Queue schedule. The jobs at the end of the LPT order that make up the last fifth
   // of the estimated time form the shared tail, cut into chunks of consecutive jobs of

@@ -36,6 +36,7 @@ struct splitkv_plan_s {
   int32_t max_rows = 0;   // max_s q_s * g
   int64_t num_jobs = 0;   // jobs of the bf16 kernels
   int64_t num_mma_jobs = 0;  // of which the matrix-path launch runs the first num_mma_jobs
+  bool mma_partial_passes = false;  // some matrix-path job has fewer than kPassTiles row tiles
   int32_t tail_start = 0;  // queue schedule: first job of the shared tail
   bool queue_default = false;  // SPLITKV_SCHED_AUTO picks the queue
   std::vector<int32_t> chunk_ptr;  // queue schedule: chunk c is jobs [chunk_ptr[c], chunk_ptr[c+1])
