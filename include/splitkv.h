@@ -149,6 +149,10 @@ typedef struct {
   int64_t num_mma_jobs;             /* jobs of at least 128 query rows (8 row tiles),    *
                                      * run by a matrix-core kernel in a launch of their  *
                                      * own before the other jobs' launch                 */
+  int32_t mma_partial_passes;       /* 1 when some such job covers fewer than 16 row    *
+                                     * tiles: that launch then runs the kernel variant   *
+                                     * whose waves may skip their second row tile; 0     *
+                                     * when every such job covers 16 (or there is none)  */
 } splitkv_plan_info;
 
 /* Device inputs. Pointers are device memory, caller-owned, read only. Strides are in

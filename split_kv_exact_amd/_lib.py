@@ -85,6 +85,7 @@ class PlanInfo(ctypes.Structure):
         ("exec_imbalance_queue_est", ctypes.c_double),
         ("auto_schedule", ctypes.c_int32),
         ("num_mma_jobs", ctypes.c_int64),
+        ("mma_partial_passes", ctypes.c_int32),
     ]
 
 

@@ -210,6 +210,7 @@ int splitkv_plan_info_get(const splitkv_plan_t* pl, splitkv_plan_info* info) {
   info->exec_imbalance_queue_est = pl->exec_queue_est;
   info->auto_schedule = pl->queue_default && pl->tail_start < pl->num_jobs ? SPLITKV_SCHED_QUEUE : SPLITKV_SCHED_STATIC;
   info->num_mma_jobs = pl->num_mma_jobs;
+  info->mma_partial_passes = pl->num_mma_jobs > 0 && pl->mma_partial_passes ? 1 : 0;
   return SPLITKV_OK;
 }
 

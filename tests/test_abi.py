@@ -209,3 +209,19 @@ def test_plan_info_sizes():
     assert inf["workspace_bytes"] >= rows * 129 * 4
     assert inf["total_q"] == 4 and inf["total_kv"] == 140
     assert inf["plan_bytes"] > 0 and inf["plan_bytes"] % 16 == 0
+
+
+@pytest.mark.parametrize("q, g, jobs, partial", [
+    ([3, 1], 2, False, 0),          # every job below 8 row tiles: no matrix-path launch
+    ([64, 125, 20], 4, True, 0),    # 256 and 500 rows: passes of 16 tiles only
+    ([300], 4, True, 1),            # 1200 rows: five passes of 15 tiles
+    ([64, 32], 4, True, 1),         # 128 rows: a pass of 8 tiles
+])
+def test_matrix_path_passes(q, g, jobs, partial):
+    """Jobs of >= 8 row tiles go to the matrix-path launch; its kernel variant with
+    per-wave tile skipping runs only when some pass has fewer than 16 tiles."""
+    kv = [max(4 * x, 64) for x in q]
+    pl = splitkv_plan(kv, q, 8 * g, 8, 128, 512, 16)
+    inf = pl.info()
+    assert (inf["num_mma_jobs"] > 0) == jobs
+    assert inf["mma_partial_passes"] == partial

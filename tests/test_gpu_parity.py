@@ -55,7 +55,18 @@ SMALL = [
     # 5, 6 and 7 row tiles per job (GQA group 16): waves 0-3 hold one or two tiles each.
     _wl("mid_tiles_d128", [700, 1200, 333], [5, 6, 7], 32, 2, 128, 256, 9),
     _wl("mid_tiles_d64", [700, 1200, 333], [5, 6, 7], 32, 2, 64, 128, 9),
+    # Matrix-path jobs whose passes all have 16 row tiles (the kernel variant without
+    # per-wave tile skipping): 256-row units, 500- and 504-row units (two passes, ragged
+    # last tile), small jobs beside them; D 128 and 64, causal and not, q = n, boosted
+    # keys.
+    _wl("full_passes_d128", [3000, 700, 1500], [64, 125, 20], 32, 8, 128, 512, 16),
+    _wl("full_passes_d64", [1100, 2000, 90], [32, 63, 3], 16, 2, 64, 256, 9, causal=False),
+    _wl("full_passes_q_equals_n", [64, 300], [64, 64], 16, 4, 128, 128, 8),
+    _wl("full_passes_boosted", [5000], [64], 64, 8, 128, 1024, 16, boost_frac=0.01),
 ]
+# Matrix-path kernel variant each case must run (mma_partial_passes of the plan info).
+MMA_PARTIAL_PASSES = {"full_passes_d128": 0, "full_passes_d64": 0, "full_passes_q_equals_n": 0,
+                      "full_passes_boosted": 0, "many_rows": 1, "multi_pass_dealt": 1, "boosted_keys": 1}
 
 
 def _run_all(wl, q, k, v, m=None):
@@ -81,6 +92,9 @@ def test_small_cases_against_full_oracle(wl):
     say(f"[gpu] small case {wl.name}")
     q, k, v = make_qkv(wl, "cuda")
     plan, ws, out_m, lse_m, out_f, lse_f = _run_all(wl, q, k, v)
+    if wl.name in MMA_PARTIAL_PASSES:
+        inf = plan.info()
+        assert inf["num_mma_jobs"] > 0 and inf["mma_partial_passes"] == MMA_PARTIAL_PASSES[wl.name]
     qh, kh, vh = widen_to_f64(q), widen_to_f64(k), widen_to_f64(v)
     O, L = attention_ref(qh, kh, vh, wl.kv_lens, wl.q_lens, wl.num_q_heads, wl.num_kv_heads, wl.causal)
     d_merge = compare(out_m.cpu().numpy(), O, lse_m.cpu().numpy(), L)
