@@ -435,7 +435,16 @@ void partial_mma_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const in
     if (!next_stage()) return false;
     unsigned char* slot = smem + (issued % NST) * C::SLOTB;
     uint32_t off[4] = {0, 0, 0, 0};
-    dma_offsets<D>(off, L, lo, kst, vst);
+    if ((L.stage + 1) * TK <= L.len) {
+      // A full stage (every stage but a block's ragged last one): the constant offsets.
+#pragma unroll
+      for (int in = 0; in < C::KVI; ++in) {
+        off[2 * in] = lo.dk[in];
+        off[2 * in + 1] = lo.dv[in];
+      }
+    } else {
+      dma_offsets<D>(off, L, lo, kst, vst);
+    }
 #pragma unroll
     for (int part = 0; part < C::NDMA; ++part) {
       const unsigned char* src = ((part & 1) ? L.vb : L.kb) + off[part];
