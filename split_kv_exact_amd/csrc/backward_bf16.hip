@@ -13,7 +13,8 @@
 //   dq:      one workgroup per forward job (a unit's KV head and up to 256 of its query
 //            rows; 4 waves when no pass has more than 128 rows, so that two workgroups
 //            share a CU, else 8): its block's keys stream through LDS in stages of 32
-//            (direct global->LDS DMA, three stages in flight); each wave keeps
+//            (direct global->LDS DMA, three stages in flight; stages below the smallest
+//            causal limit of a wave's rows skip the causal test); each wave keeps
 //            Q, dO and its dQ part of two 16-row tiles in registers. Scores are computed
 //            transposed as in the forward (S^T = K Q^T), dP^T = V dO^T the same way, and
 //            dQ^T += K^T dS^T with K^T read by transposing LDS loads. The part goes to the
@@ -22,9 +23,11 @@
 //            (one wavefront per row);
 //   dkv:     one workgroup of 4 waves per (sequence, KV head, 64-key tile); a wave holds
 //            its 16 keys' K and V rows in registers and dK^T, dV^T accumulators, and the
-//            query rows that see the tile stream through LDS 32 at a time (direct
-//            global->LDS DMA, one chunk ahead): S = Q K^T, dP = dO V^T, then dV^T += dO^T P
-//            and dK^T += Q^T dS with Q^T and dO^T read by transposing loads. Kept at 160
+//            query rows that see the tile stream through LDS 32 at a time, with their LSE
+//            and D (direct global->LDS DMA, two chunks ahead, three buffers, one barrier
+//            per chunk; when g divides 32 a lane's loads are a per-chunk scalar base plus
+//            constant offsets): S = Q K^T, dP = dO V^T, then dV^T += dO^T P and
+//            dK^T += Q^T dS with Q^T and dO^T read by transposing loads. Kept at 168
 //            VGPRs or fewer (three workgroups per CU). dK and dV are written once.
 // P and dS enter the matrix cores rounded to bf16 (as P does in the forward); all sums
 // are fp32.
@@ -155,16 +158,31 @@ __global__ __launch_bounds__(W * 64, 2) void dq_kernel(BwdArgs a) {
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k) + 2 * (j.kv_tok * a.k_st + int64_t(j.kv) * a.k_sh);
   const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v) + 2 * (j.kv_tok * a.v_st + int64_t(j.kv) * a.v_sh);
   int srow[PW], kcc[PW], vcc[PW];
+  uint32_t koff[PW], voff[PW];  // this lane's bytes of a full stage, from its first key
 #pragma unroll
   for (int u = 0; u < PW; ++u) {
     const int p = (wave * PW + u) * 64 + lane;
     srow[u] = p / C::CH;
     kcc[u] = swz_tr<C::CH>(srow[u], p % C::CH);
     vcc[u] = swz_row<C::CH>(srow[u], p % C::CH);
+    koff[u] = uint32_t(srow[u]) * uint32_t(2 * a.k_st) + 16u * kcc[u];
+    voff[u] = uint32_t(srow[u]) * uint32_t(2 * a.v_st) + 16u * vcc[u];
   }
   auto issue_stage = [&](int st) {
     if (wave * PW >= NI) return;
     const int buf = st % DQ_BUFS;
+    if ((st + 1) * DQ_KEYS <= j.len) {
+      // A full stage: the stage's first key plus the constant per-lane offsets.
+      const unsigned char* ks = kbase + int64_t(st * DQ_KEYS) * (2 * a.k_st);
+      const unsigned char* vs = vbase + int64_t(st * DQ_KEYS) * (2 * a.v_st);
+#pragma unroll
+      for (int u = 0; u < PW; ++u) {
+        const int gi = wave * PW + u;
+        __builtin_amdgcn_global_load_lds(ks + koff[u], (lds_void*)(L.k[buf] + gi * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vs + voff[u], (lds_void*)(L.v[buf] + gi * 1024), 16, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < PW; ++u) {
       const int key = min(st * DQ_KEYS + srow[u], j.len - 1);  // past the block: its last key (masked)
@@ -187,6 +205,10 @@ __global__ __launch_bounds__(W * 64, 2) void dq_kernel(BwdArgs a) {
     for (int dt = 0; dt < C::DT; ++dt) ok_tr[dt] = r * C::ROWB + 16 * swz_tr<C::CH>(r, 2 * dt + (cc >> 1)) + 8 * (cc & 1);
   }
 
+  // Keys up to the smallest limit of the wave's rows (its first row) are visible to all
+  // of them: stages that end there need no causal test.
+  const int r_first = min((j.tile_lo + min(wave, j.tile_n - 1)) * 16, j.rows - 1);
+  const int wave_min_lim = min(j.lim0 + r_first / a.g, j.len - 1);
   const int nst = j.nst * (kStageKeys / DQ_KEYS);  // the job's stages of visible keys, in 32-key steps
   for (int st = 0; st < DQ_BUFS - 1 && st < nst; ++st) issue_stage(st);
   for (int st = 0; st < nst; ++st) {
@@ -197,6 +219,7 @@ __global__ __launch_bounds__(W * 64, 2) void dq_kernel(BwdArgs a) {
     const unsigned kb = lds_addr(L.k[buf]), vb = lds_addr(L.v[buf]);
     {
       const int key0 = st * DQ_KEYS;  // block key of the stage's first key
+      const bool all_vis = key0 + DQ_KEYS - 1 <= wave_min_lim;
       if (nt > 0) {
         // Per 16-key tile: S^T and dP^T, then dS^T = P^T (dP^T - D) with
         // P^T = 2^(s c - LSE log2 e); entry e of tile tt is block key key0 + 16 tt + 4 G + e.
@@ -220,11 +243,17 @@ __global__ __launch_bounds__(W * 64, 2) void dq_kernel(BwdArgs a) {
                 y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dc], dop[t][dc], y, 0, 0, 0);
               }
             }
+            if (all_vis) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int key = key0 + 16 * tt + 4 * G + e;
-              const float pr = key <= lim[t] ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c, -lsec[t])) : 0.f;
-              ds[t][tt][e] = pr * (y[e] - dd[t]);
+              for (int e = 0; e < 4; ++e)
+                ds[t][tt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c, -lsec[t])) * (y[e] - dd[t]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int key = key0 + 16 * tt + 4 * G + e;
+                const float pr = key <= lim[t] ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c, -lsec[t])) : 0.f;
+                ds[t][tt][e] = pr * (y[e] - dd[t]);
+              }
             }
           }
         }
@@ -304,15 +333,15 @@ __global__ __launch_bounds__(256) void dqsum_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- dK, dV per key tile
 constexpr int KV_WAVES = 4;
-constexpr int RCH = 32;  // query rows per chunk
+constexpr int RCH = 32;     // query rows per chunk
+constexpr int KV_BUFS = 3;  // chunk buffers: the chunk computed and two in flight
 
 template <int D>
 struct KvLds {
-  unsigned char q[2][RCH * BCfg<D>::ROWB];   // Q rows, stored for row and transposing reads
-  unsigned char g[2][RCH * BCfg<D>::ROWB];   // dO rows, likewise
-  float lsec[2][RCH];                         // LSE * log2(e) (+inf for rows past the last)
-  float dd[2][RCH];                           // D_i
-  int pos[2][RCH];                            // position of the row's query token
+  unsigned char q[KV_BUFS][RCH * BCfg<D>::ROWB];   // Q rows, stored for row and transposing reads
+  unsigned char g[KV_BUFS][RCH * BCfg<D>::ROWB];   // dO rows, likewise
+  float lse[KV_BUFS][RCH];                          // the rows' LSE (natural log)
+  float dd[KV_BUFS][RCH];                           // D_i
 };
 
 template <int D>
@@ -357,29 +386,72 @@ __global__ __launch_bounds__(256, 3) void dkv_kernel(BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Rows that see some key of the tile: query tokens i >= k0 - (n - q) when causal.
+  // Rows that see some key of the tile: query tokens i >= k0 - (n - q) when causal. Row r
+  // (token r / g) sees this lane's key when r >= r_vis = g (key - (n - q)).
   const int q = sq.q;
   const int64_t i0 = a.causal ? max<int64_t>(0, k0 - (n - q)) : 0;
   const int r_begin = int(i0) * a.g;
   const int nchunk = r_begin < rows ? (rows - r_begin + RCH - 1) / RCH : 0;
+  const int r_vis = a.causal ? int(min<int64_t>(max<int64_t>(int64_t(a.g) * (key - (n - q)), 0), rows)) : 0;
+  const bool key_in = key < n;
 
-  // Chunk loads: Q and dO rows go straight to LDS (global_load_lds_dwordx4, 1 KiB per
-  // instruction, lane l to byte 16 l of it). LDS position p of a tile (16-byte units)
-  // is row p / CH, slot p % CH; the slot holds the row's chunk swz_tr(row, slot) (the
-  // swizzle is an XOR, its own inverse), so each lane loads the chunk its position
-  // needs. The per-row LSE, D and position travel through registers (threads < RCH).
+  // Chunk loads, all by direct global->LDS DMA: Q and dO rows (1 KiB per instruction,
+  // lane l to byte 16 l of it; LDS position p of a tile (16-byte units) is row p / CH,
+  // slot p % CH, and holds the row's chunk swz_tr(row, slot), so each lane loads the chunk
+  // its position needs), and the rows' LSE and D (wave 0, 4 bytes per lane). Rows past
+  // the last re-read it (finite data, not visible).
   constexpr int TILE_INST = RCH * C::ROWB / 1024;      // instructions per tile
   constexpr int PER_WAVE = TILE_INST / KV_WAVES;       // per wave, per tensor
   static_assert(PER_WAVE * KV_WAVES == TILE_INST, "chunk tile split");
-  float r_l = 0.f, r_d = 0.f;
-  int r_p = 0;
+  // Vector-memory instructions this wave issues per chunk.
+  const int per_chunk = 2 * PER_WAVE + (wave == 0 ? 2 : 0);
   auto row_src = [&](int r, int64_t& tok, int64_t& head) {
     const int i = r / a.g, hl = r - i * a.g;
     tok = sq.q_base + i;
     head = int64_t(kv) * a.g + hl;
   };
+  // When g divides the chunk's row count, a lane's row of a chunk is the same (token,
+  // head) offset from the chunk's first row in every chunk: the loads are a scalar base
+  // per chunk plus per-lane constant offsets. Otherwise, and for a chunk that runs past
+  // the last row, each lane computes its row's address.
+  const bool fixed = RCH % a.g == 0;
+  uint32_t fq[PER_WAVE], fg[PER_WAVE], fs = 0;
+#pragma unroll
+  for (int u = 0; u < PER_WAVE; ++u) {
+    const int p = (wave * PER_WAVE + u) * 64 + lane;
+    const int row = p / C::CH, cc = swz_tr<C::CH>(row, p % C::CH);
+    const int i = row / a.g, hl = row - i * a.g;
+    fq[u] = uint32_t(2 * (i * a.q_st + hl * a.q_sh) + 16 * cc);
+    fg[u] = uint32_t(2 * (i * a.do_st + hl * a.do_sh) + 16 * cc);
+  }
+  fs = uint32_t((lane / a.g) * a.Hq + lane % a.g);
+  // Addresses of the first row of the next chunk to load (chunks load in order), and
+  // their steps per chunk (RCH / g tokens).
+  const int64_t tok0 = sq.q_base + r_begin / a.g, head0 = int64_t(kv) * a.g;
+  const unsigned char* nq = reinterpret_cast<const unsigned char*>(a.q) + 2 * (tok0 * a.q_st + head0 * a.q_sh);
+  const unsigned char* ng = reinterpret_cast<const unsigned char*>(a.dout) + 2 * (tok0 * a.do_st + head0 * a.do_sh);
+  int64_t ns = tok0 * a.Hq + head0;
+  const int tstep = fixed ? RCH / a.g : 0;
+  const int64_t dq_step = 2 * int64_t(tstep) * a.q_st, dg_step = 2 * int64_t(tstep) * a.do_st,
+                ds_step = int64_t(tstep) * a.Hq;
   auto load_chunk = [&](int ch, int buf) {
     const int rb = r_begin + ch * RCH;
+    if (fixed && rb + RCH <= rows) {
+#pragma unroll
+      for (int u = 0; u < PER_WAVE; ++u) {
+        const int gi = wave * PER_WAVE + u;
+        __builtin_amdgcn_global_load_lds(nq + fq[u], (lds_void*)(L.q[buf] + gi * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(ng + fg[u], (lds_void*)(L.g[buf] + gi * 1024), 16, 0, 0);
+      }
+      if (wave == 0 && lane < RCH) {
+        __builtin_amdgcn_global_load_lds(a.lse + ns + fs, (lds_void*)L.lse[buf], 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(a.ws_d + ns + fs, (lds_void*)L.dd[buf], 4, 0, 0);
+      }
+      nq += dq_step;
+      ng += dg_step;
+      ns += ds_step;
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
       const int gi = wave * PER_WAVE + u;
@@ -394,20 +466,11 @@ __global__ __launch_bounds__(256, 3) void dkv_kernel(BwdArgs a) {
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char*>(a.dout) + 2 * (tok * a.do_st + head * a.do_sh) + 16 * cc,
                                        (lds_void*)(L.g[buf] + gi * 1024), 16, 0, 0);
     }
-    if (threadIdx.x < RCH) {
-      const int r = rb + threadIdx.x;
+    if (wave == 0 && lane < RCH) {
       int64_t tok, head;
-      row_src(min(r, rows - 1), tok, head);
-      r_l = a.lse[tok * a.Hq + head];  // scaled when stored: no use of the loaded value before then
-      r_d = a.ws_d[tok * a.Hq + head];
-      r_p = r < rows ? int(n - q + (min(r, rows - 1) / a.g)) : -1;
-    }
-  };
-  auto store_chunk = [&](int buf) {
-    if (threadIdx.x < RCH) {
-      L.lsec[buf][threadIdx.x] = r_p >= 0 ? r_l * LOG2E : __builtin_huge_valf();
-      L.dd[buf][threadIdx.x] = r_d;
-      L.pos[buf][threadIdx.x] = r_p;
+      row_src(min(rb + lane, rows - 1), tok, head);
+      __builtin_amdgcn_global_load_lds(a.lse + (tok * a.Hq + head), (lds_void*)L.lse[buf], 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.ws_d + (tok * a.Hq + head), (lds_void*)L.dd[buf], 4, 0, 0);
     }
   };
   // Lane offsets within a 16-row tile of a chunk: row reads (lane: row li, dims 8G + 32dc)
@@ -421,13 +484,19 @@ __global__ __launch_bounds__(256, 3) void dkv_kernel(BwdArgs a) {
     for (int dt = 0; dt < C::DT; ++dt) o_tr[dt] = r * C::ROWB + 16 * swz_tr<C::CH>(r, 2 * dt + (cc >> 1)) + 8 * (cc & 1);
   }
 
+  // The K and V operands first (a compiler-visible wait), so that no wait for them
+  // drains the chunk DMA below.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   if (nchunk > 0) load_chunk(0, 0);
+  if (nchunk > 1) load_chunk(1, 1);
+  int buf = 0;
   for (int ch = 0; ch < nchunk; ++ch) {
-    const int buf = ch & 1;
-    store_chunk(buf);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's part of chunk ch has landed
-    __syncthreads();
-    if (ch + 1 < nchunk) load_chunk(ch + 1, buf ^ 1);
+    // Chunk ch has landed for this wave once only chunk ch + 1's loads may be pending;
+    // the barrier makes every wave's part visible, and every wave is past its reads of
+    // the buffer that chunk ch + 2 now refills (last read for chunk ch - 1).
+    dq_wait_barrier(ch + 1 < nchunk ? per_chunk : 0);
+    if (ch + 2 < nchunk) load_chunk(ch + 2, buf == 0 ? 2 : buf - 1);
+    const int rb = r_begin + ch * RCH;
     const unsigned qb = lds_addr(L.q[buf]), gb = lds_addr(L.g[buf]);
     // S and dP for the chunk's two 16-row tiles (lane: key li, rows 16 t + 4 G + e).
     f32x4 sv[2], pv[2];
@@ -451,17 +520,20 @@ __global__ __launch_bounds__(256, 3) void dkv_kernel(BwdArgs a) {
       for (int dc = 0; dc < C::DC; ++dc) y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[dc], vt[dc], y, 0, 0, 0);
       pv[t] = y;
     }
-    // P and dS (rows past the last have LSE = +inf, so P = 0).
+    // P and dS; a row that does not see the key (or lies past the last row) gives 0.
     float pr[2][4], ds[2][4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&L.lse[buf][16 * t + 4 * G]);
+      const f32x4 dd4 = *reinterpret_cast<const f32x4*>(&L.dd[buf][16 * t + 4 * G]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int rr = 16 * t + 4 * G + e;
-        const bool vis = key < n && (!a.causal || key <= L.pos[buf][rr]);
-        pr[t][e] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t][e], c, -L.lsec[buf][rr])) : 0.f;
-        ds[t][e] = pr[t][e] * (pv[t][e] - L.dd[buf][rr]);
+        const int r = rb + 16 * t + 4 * G + e;
+        const bool vis = key_in && r < rows && r >= r_vis;
+        pr[t][e] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t][e], c, -LOG2E * lse4[e])) : 0.f;
+        ds[t][e] = pr[t][e] * (pv[t][e] - dd4[e]);
       }
+    }
     const bf16x8 pb = {(__bf16)pr[0][0], (__bf16)pr[0][1], (__bf16)pr[0][2], (__bf16)pr[0][3],
                        (__bf16)pr[1][0], (__bf16)pr[1][1], (__bf16)pr[1][2], (__bf16)pr[1][3]};
     const bf16x8 db = {(__bf16)ds[0][0], (__bf16)ds[0][1], (__bf16)ds[0][2], (__bf16)ds[0][3],
@@ -493,7 +565,7 @@ __global__ __launch_bounds__(256, 3) void dkv_kernel(BwdArgs a) {
         dk[half * DH + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[d], hi[d], 0, 1, 2, 3, 4, 5, 6, 7)), db, dk[half * DH + d], 0, 0, 0);
     }
-    __syncthreads();  // every wave is done with this buffer before it is refilled
+    buf = buf == KV_BUFS - 1 ? 0 : buf + 1;
   }
   // Store (lane: key li, dims 16 dt + 4 G .. + 3); keys past the sequence are not stored.
   if (key < n) {
