@@ -49,6 +49,11 @@ CASES = [
     _wl("two_row_passes", [2048], [300], 32, 8, 128, 512, 8),
     _wl("boosted_keys", [3000, 1500], [16, 1], 64, 8, 128, 512, 32, boost_frac=0.01),
     _wl("mid_tiles", [700, 1200, 333], [5, 6, 7], 32, 2, 128, 256, 9),
+    # Query heads per KV head that do not divide the 32-row chunk of the dK/dV kernel
+    # (every chunk computes its rows' addresses): g = 3, and g = 64 (a chunk is half of
+    # one query token's rows).
+    _wl("group_of_3", [900, 300, 41], [7, 3, 2], 6, 2, 128, 256, 5),
+    _wl("group_of_64", [500, 130], [3, 2], 64, 1, 64, 128, 4),
 ]
 
 

@@ -63,6 +63,9 @@ SMALL = [
     _wl("full_passes_d64", [1100, 2000, 90], [32, 63, 3], 16, 2, 64, 256, 9, causal=False),
     _wl("full_passes_q_equals_n", [64, 300], [64, 64], 16, 4, 128, 128, 8),
     _wl("full_passes_boosted", [5000], [64], 64, 8, 128, 1024, 16, boost_frac=0.01),
+    # A GQA group that is not a power of two (g = 3) and one of 64 heads per KV head.
+    _wl("group_of_3", [900, 300, 41], [7, 3, 2], 6, 2, 128, 256, 5),
+    _wl("group_of_64", [500, 130], [3, 2], 64, 1, 64, 128, 4),
 ]
 # Matrix-path kernel variant each case must run (mma_partial_passes of the plan info).
 MMA_PARTIAL_PASSES = {"full_passes_d128": 0, "full_passes_d64": 0, "full_passes_q_equals_n": 0,
