@@ -33,13 +33,14 @@ if ROOT not in sys.path:
 METRIC = "split-KV attention+merge effective HBM GB/s & TFLOP/s, % of MI355X roofline"
 
 
-KERNEL_SOURCES = ("partial_bf16.hip", "partial_mma.hip", "partial_f32.hip", "merge.hip", "abi.cpp", "plan.cpp",
+KERNEL_SOURCES = ("partial_bf16.hip", "partial_mma.hip", "partial_f32.hip", "abi.cpp", "plan.cpp",
                   "kernels.hpp", "plan_image.hpp", "lds_tiles.hpp")
 
 
 def _kernel_sha(csrc: str | None = None) -> str:
-    """Hash of the forward path's sources with comments and blank space removed, so that
-    an edit of comments alone does not mark the committed counter runs as stale."""
+    """Hash of the partial-attention launch's sources (the kernels, the plan and the
+    launch code; the merge is a separate kernel) with comments and blank space removed,
+    so that an edit of comments alone does not mark the committed counter runs as stale."""
     csrc = csrc or os.path.join(ROOT, "split_kv_exact_amd", "csrc")
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:

@@ -25,11 +25,12 @@ def test_source_hash_ignores_comments_only(tmp_path):
         shutil.copy(os.path.join(csrc, f), tmp_path / f)
     base = bench._kernel_sha(str(tmp_path))
     assert base == bench._kernel_sha(csrc)
-    p = tmp_path / "merge.hip"
+    p = tmp_path / "partial_mma.hip"
     text = p.read_text()
     p.write_text("// a new comment\n" + text.replace("\n", "\n  \n", 3) + "/* trailing\n block */\n")
     assert bench._kernel_sha(str(tmp_path)) == base
-    p.write_text(text.replace("UNROLL = 16", "UNROLL = 8"))
+    assert "constexpr int NST = 4;" in text
+    p.write_text(text.replace("constexpr int NST = 4;", "constexpr int NST = 3;"))
     assert bench._kernel_sha(str(tmp_path)) != base
 
 
