@@ -278,7 +278,7 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
         j.tile_lo = t0;
         j.tile_n = tn;
         t0 += tn;
-        const int32_t rmax = std::min(r.rows, (t0 + j.tile_n) * 16) - 1;
+        const int32_t rmax = std::min(r.rows, t0 * 16) - 1;  // the pass's last row
         const int64_t tmax = std::min<int64_t>(len - 1, int64_t(lim0) + rmax / g);
         j.nst = tmax < 0 ? 1 : int32_t(tmax / kStageKeys) + 1;
         const int32_t wr_log = j.tile_n >= 8 ? 3 : j.tile_n >= 4 ? 2 : j.tile_n >= 2 ? 1 : 0;
