@@ -304,6 +304,7 @@ struct State {
   f32x4 ls[RTW];   // sum of the bf16-rounded p of this lane's row (every entry equal)
   float m[RTW];    // running reference max of raw scores (row of this lane)
   float thr[RTW];  // scores above this move the reference: m + RESCALE_LOG2 / c
+  float pthr[RTW]; // a lane whose step sum of p exceeds this looks for such scores
   float nmc[RTW];  // -m * c (0 while m = -inf)
   float l[RTW];    // this lane's share of the row sum of the fp32 p
   int lim[RTW];    // last visible block key of this lane's row
@@ -320,6 +321,7 @@ __device__ __forceinline__ void reset(State<D>& st) {
     for (int dt = 0; dt < Cfg<D>::DT; ++dt) st.o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.m[t] = NEG_INF;
     st.thr[t] = NEG_INF;
+    st.pthr[t] = -1.f;
     st.nmc[t] = 0.f;
     st.l[t] = 0.f;
     st.ls[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -331,6 +333,7 @@ __device__ __forceinline__ void reset(State<D>& st) {
 // reach 2^RESCALE_LOG2, which fp32 and bf16 hold exactly in range. O, l and LSE all use
 // the same reference, so the result does not depend on when it moved.
 constexpr float RESCALE_LOG2 = 8.f;
+constexpr float PSUM_RESCAN = 128.f;  // 2^(RESCALE_LOG2 - 1)
 
 // One online-softmax step of this wave: its nt row tiles against 32 keys (block keys
 // key0..key0+31), in three phases: scores (matrix cores), softmax (vector ALUs),
@@ -366,8 +369,8 @@ __device__ __forceinline__ void step_scores(Scores<D>& S, const State<D>& st, in
   }
 }
 
-// Mask, running max, p = 2^(s*c - m*c) rounded to bf16 for the P V product; the row
-// sum of the fp32 p goes to l.
+// Mask, p = 2^(s*c - m*c) rounded to bf16 for the P V product, the reference max moved
+// when a score rises far enough above it; the row sum of the fp32 p goes to l.
 template <int D>
 __device__ __forceinline__ void step_softmax(Scores<D>& S, State<D>& st, int nt, bf16x4 (&p)[RTW][NT], int key0,
                                              bool need_mask, float c, float inv_c) {
@@ -386,33 +389,44 @@ __device__ __forceinline__ void step_softmax(Scores<D>& S, State<D>& st, int nt,
           for (int e = 0; e < 4; ++e)
             if (16 * tt + e > d) S.s[t][tt][e] = NEG_INF;
       }
-      float mx = fmaxf(fmaxf(S.s[t][0][0], S.s[t][0][1]), fmaxf(S.s[t][0][2], S.s[t][0][3]));
-      mx = fmaxf(mx, fmaxf(fmaxf(S.s[t][1][0], S.s[t][1][1]), fmaxf(S.s[t][1][2], S.s[t][1][3])));
-      // Move the reference (and rescale) only on a large increase; -inf -> finite always
-      // moves. The test first uses this lane's own scores: only when some lane would move
-      // is the row max formed across the row's four lanes (rare after the first step).
-      if (__any(mx > st.thr[t])) {
+      // p first, against the current reference. A score above thr gives p > 2^RESCALE_LOG2,
+      // so its lane's sum of p exceeds pthr = 2^(RESCALE_LOG2 - 1) whatever the rounding:
+      // only then is the row max formed across the row's four lanes, the reference moved
+      // (and O, l rescaled) if the max exceeds thr, and p taken again. While m = -inf,
+      // pthr = -1 sends every lane there (-inf -> finite always moves). The reference so
+      // moves exactly where a per-step row max would move it.
+      float pe[NT][4];
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pe[tt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S.s[t][tt][e], c, st.nmc[t]));
+      float ps = ((pe[0][0] + pe[0][1]) + (pe[0][2] + pe[0][3])) + ((pe[1][0] + pe[1][1]) + (pe[1][2] + pe[1][3]));
+      if (__any(ps > st.pthr[t])) {
+        float mx = fmaxf(fmaxf(S.s[t][0][0], S.s[t][0][1]), fmaxf(S.s[t][0][2], S.s[t][0][3]));
+        mx = fmaxf(mx, fmaxf(fmaxf(S.s[t][1][0], S.s[t][1][1]), fmaxf(S.s[t][1][2], S.s[t][1][3])));
         mx = max4(mx);
         if (mx > st.thr[t]) {
           const float alpha = st.m[t] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((st.m[t] - mx) * c);
           st.m[t] = mx;
           st.thr[t] = mx + RESCALE_LOG2 * inv_c;
+          st.pthr[t] = PSUM_RESCAN;
           st.nmc[t] = -mx * c;
           st.l[t] *= alpha;
           st.ls[t] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < C::DT; ++dt) st.o[t][dt] *= alpha;
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pe[tt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S.s[t][tt][e], c, st.nmc[t]));
+          ps = ((pe[0][0] + pe[0][1]) + (pe[0][2] + pe[0][3])) + ((pe[1][0] + pe[1][1]) + (pe[1][2] + pe[1][3]));
         }
       }
-      float pe[NT][4];
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pe[tt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S.s[t][tt][e], c, st.nmc[t]));
-          p[t][tt][e] = (__bf16)pe[tt][e];
-        }
-      st.l[t] += ((pe[0][0] + pe[0][1]) + (pe[0][2] + pe[0][3])) + ((pe[1][0] + pe[1][1]) + (pe[1][2] + pe[1][3]));
+        for (int e = 0; e < 4; ++e) p[t][tt][e] = (__bf16)pe[tt][e];
+      st.l[t] += ps;
     }
   }
 }

@@ -48,6 +48,7 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.69314718055994531f;
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr float RESCALE_LOG2 = 8.f;
+constexpr float PSUM_RESCAN = 128.f;  // 2^(RESCALE_LOG2 - 1)
 static_assert(TK == 64, "two 32-key steps per stage");
 static_assert(AHEAD <= NST - 1, "a slot is refilled after the barrier that ends its last read");
 
@@ -207,6 +208,7 @@ struct State {
   f32x4 ls[2];   // sum of the bf16-rounded p of this lane's row (every entry equal)
   float m[2];    // running reference max of raw scores
   float thr[2];  // scores above this move the reference: m + RESCALE_LOG2 / c
+  float pthr[2]; // a lane whose step sum of p exceeds this looks for such scores
   float nmc[2];  // -m * c (0 while m = -inf)
   float l[2];    // this lane's share of the row sum of the fp32 p
   int lim[2];    // last visible block key of this lane's row
@@ -220,6 +222,7 @@ __device__ __forceinline__ void reset(State<D>& st) {
     for (int dt = 0; dt < Cfg<D>::DT; ++dt) st.o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.m[t] = NEG_INF;
     st.thr[t] = NEG_INF;
+    st.pthr[t] = -1.f;
     st.nmc[t] = 0.f;
     st.l[t] = 0.f;
     st.ls[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -274,30 +277,43 @@ __device__ __forceinline__ void softmax(f32x4 (&s)[2][2], State<D>& st, bf16x4 (
         for (int e = 0; e < 4; ++e)
           if (16 * tt + e > d) s[t][tt][e] = NEG_INF;
     }
-    float mx = fmaxf(fmaxf(s[t][0][0], s[t][0][1]), fmaxf(s[t][0][2], s[t][0][3]));
-    mx = fmaxf(mx, fmaxf(fmaxf(s[t][1][0], s[t][1][1]), fmaxf(s[t][1][2], s[t][1][3])));
-    if (__any(mx > st.thr[t])) {
+    // p first, against the current reference. A score above thr gives p > 2^RESCALE_LOG2,
+    // so its lane's sum of p exceeds pthr = 2^(RESCALE_LOG2 - 1) whatever the rounding:
+    // only then is the row maximum formed (and the reference moved, and p taken again).
+    // While m = -inf, pthr = -1 sends every lane there. The reference therefore moves
+    // exactly where a row maximum above thr moves it, without a maximum per step.
+    float pe[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pe[tt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][tt][e], c, st.nmc[t]));
+    float ps = ((pe[0][0] + pe[0][1]) + (pe[0][2] + pe[0][3])) + ((pe[1][0] + pe[1][1]) + (pe[1][2] + pe[1][3]));
+    if (__any(ps > st.pthr[t])) {
+      float mx = fmaxf(fmaxf(s[t][0][0], s[t][0][1]), fmaxf(s[t][0][2], s[t][0][3]));
+      mx = fmaxf(mx, fmaxf(fmaxf(s[t][1][0], s[t][1][1]), fmaxf(s[t][1][2], s[t][1][3])));
       mx = max4(mx);
       if (mx > st.thr[t]) {
         const float alpha = st.m[t] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((st.m[t] - mx) * c);
         st.m[t] = mx;
         st.thr[t] = mx + RESCALE_LOG2 * inv_c;
+        st.pthr[t] = PSUM_RESCAN;
         st.nmc[t] = -mx * c;
         st.l[t] *= alpha;
         st.ls[t] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < Cfg<D>::DT; ++dt) st.o[t][dt] *= alpha;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pe[tt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][tt][e], c, st.nmc[t]));
+        ps = ((pe[0][0] + pe[0][1]) + (pe[0][2] + pe[0][3])) + ((pe[1][0] + pe[1][1]) + (pe[1][2] + pe[1][3]));
       }
     }
-    float pe[2][4];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pe[tt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][tt][e], c, st.nmc[t]));
-        p[t][tt][e] = (__bf16)pe[tt][e];
-      }
-    st.l[t] += ((pe[0][0] + pe[0][1]) + (pe[0][2] + pe[0][3])) + ((pe[1][0] + pe[1][1]) + (pe[1][2] + pe[1][3]));
+      for (int e = 0; e < 4; ++e) p[t][tt][e] = (__bf16)pe[tt][e];
+    st.l[t] += ps;
   }
 }
 
