@@ -285,8 +285,8 @@ typedef struct {
  *   D_i = <dO_i, O_i>, P = e^(scale q.k - LSE), dS = P (dO.v - D),
  *   dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO,
  * with dK and dV summed over the query heads of each KV head. bf16 inputs only;
- * gradients fp32. The workspace (splitkv_plan_info.workspace_bytes) holds the dQ parts
- * and D. The fields schedule and worker_clock of in are not used.
+ * gradients fp32. The workspace (splitkv_plan_info.workspace_bytes) holds the dQ parts,
+ * D and the LSE in base 2. The fields schedule and worker_clock of in are not used.
  * Errors: INVALID_ARG (NULL or misaligned pointers, bad strides), UNSUPPORTED (fp32
  * inputs, head_dim other than 64 or 128, bf16 strides beyond 2^24), WORKSPACE, HIP. */
 int splitkv_attn_backward(const splitkv_plan_t *plan, const void *dev_plan, const splitkv_inputs *in,

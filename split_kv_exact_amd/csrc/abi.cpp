@@ -341,6 +341,7 @@ int splitkv_attn_backward(const splitkv_plan_t* pl, const void* dev_plan, const 
   b.dv = gr->dv;
   b.ws_dq = ws;
   b.ws_d = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + pl->ws_lse_offset);
+  b.ws_l2 = b.ws_d + pl->total_q * pl->Hq;
   b.seqs = reinterpret_cast<const splitkv::SeqRec*>(base + pl->layout.seqs);
   b.S = pl->S;
   b.jobs = reinterpret_cast<const splitkv::JobRec*>(base + pl->layout.jobs);

@@ -60,6 +60,8 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // ---------------------------------------------------------------- D_i = <dO_i, O_i>
+// and the row's LSE in base 2 (LSE_i * log2 e, the product the dK/dV kernel would
+// otherwise form for every (row, key) pair).
 template <int D>
 __global__ __launch_bounds__(256) void rowdot_kernel(BwdArgs a) {
   const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);  // i * Hq + h
@@ -72,7 +74,10 @@ __global__ __launch_bounds__(256) void rowdot_kernel(BwdArgs a) {
 #pragma unroll
   for (int k = 0; k < D / 64; ++k) s += float(dop[lane + 64 * k]) * op[lane + 64 * k];
   s = wave_sum(s);
-  if (lane == 0) a.ws_d[row] = s;
+  if (lane == 0) {
+    a.ws_d[row] = s;
+    a.ws_l2[row] = LOG2E * a.lse[row];
+  }
 }
 
 // ---------------------------------------------------------------- dQ parts per job
@@ -340,7 +345,7 @@ template <int D>
 struct KvLds {
   unsigned char q[KV_BUFS][RCH * BCfg<D>::ROWB];   // Q rows, stored for row and transposing reads
   unsigned char g[KV_BUFS][RCH * BCfg<D>::ROWB];   // dO rows, likewise
-  float lse[KV_BUFS][RCH];                          // the rows' LSE (natural log)
+  float lse[KV_BUFS][RCH];                          // the rows' LSE * log2 e
   float dd[KV_BUFS][RCH];                           // D_i
 };
 
@@ -394,6 +399,12 @@ __global__ __launch_bounds__(256, 3) void dkv_kernel(BwdArgs a) {
   const int nchunk = r_begin < rows ? (rows - r_begin + RCH - 1) / RCH : 0;
   const int r_vis = a.causal ? int(min<int64_t>(max<int64_t>(int64_t(a.g) * (key - (n - q)), 0), rows)) : 0;
   const bool key_in = key < n;
+  // The same for the wave's last key (wave-uniform): a chunk whose rows all exist and
+  // start at or past r_vis_last is seen by all 16 keys of the wave, and needs no test.
+  const int64_t key_last = k0 + 16 * wave + 15;
+  const bool keys_in = key_last < n;
+  const int r_vis_last =
+      a.causal ? int(min<int64_t>(max<int64_t>(int64_t(a.g) * (key_last - (n - q)), 0), rows)) : 0;
 
   // Chunk loads, all by direct global->LDS DMA: Q and dO rows (1 KiB per instruction,
   // lane l to byte 16 l of it; LDS position p of a tile (16-byte units) is row p / CH,
@@ -437,15 +448,22 @@ __global__ __launch_bounds__(256, 3) void dkv_kernel(BwdArgs a) {
   auto load_chunk = [&](int ch, int buf) {
     const int rb = r_begin + ch * RCH;
     if (fixed && rb + RCH <= rows) {
+      // Each load is a uniform base plus a 32-bit lane offset. The offsets pass through
+      // an empty asm so that the compiler does not keep base + offset as a 64-bit lane
+      // address across the loop (registers this kernel does not have).
 #pragma unroll
       for (int u = 0; u < PER_WAVE; ++u) {
         const int gi = wave * PER_WAVE + u;
-        __builtin_amdgcn_global_load_lds(nq + fq[u], (lds_void*)(L.q[buf] + gi * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(ng + fg[u], (lds_void*)(L.g[buf] + gi * 1024), 16, 0, 0);
+        uint32_t oq = fq[u], og = fg[u];
+        asm volatile("" : "+v"(oq), "+v"(og));
+        __builtin_amdgcn_global_load_lds(nq + oq, (lds_void*)(L.q[buf] + gi * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(ng + og, (lds_void*)(L.g[buf] + gi * 1024), 16, 0, 0);
       }
       if (wave == 0 && lane < RCH) {
-        __builtin_amdgcn_global_load_lds(a.lse + ns + fs, (lds_void*)L.lse[buf], 4, 0, 0);
-        __builtin_amdgcn_global_load_lds(a.ws_d + ns + fs, (lds_void*)L.dd[buf], 4, 0, 0);
+        uint32_t os = 4 * fs;
+        asm volatile("" : "+v"(os));
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char*>(a.ws_l2 + ns) + os, (lds_void*)L.lse[buf], 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char*>(a.ws_d + ns) + os, (lds_void*)L.dd[buf], 4, 0, 0);
       }
       nq += dq_step;
       ng += dg_step;
@@ -469,7 +487,7 @@ __global__ __launch_bounds__(256, 3) void dkv_kernel(BwdArgs a) {
     if (wave == 0 && lane < RCH) {
       int64_t tok, head;
       row_src(min(rb + lane, rows - 1), tok, head);
-      __builtin_amdgcn_global_load_lds(a.lse + (tok * a.Hq + head), (lds_void*)L.lse[buf], 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.ws_l2 + (tok * a.Hq + head), (lds_void*)L.lse[buf], 4, 0, 0);
       __builtin_amdgcn_global_load_lds(a.ws_d + (tok * a.Hq + head), (lds_void*)L.dd[buf], 4, 0, 0);
     }
   };
@@ -521,18 +539,29 @@ __global__ __launch_bounds__(256, 3) void dkv_kernel(BwdArgs a) {
       pv[t] = y;
     }
     // P and dS; a row that does not see the key (or lies past the last row) gives 0.
+    // Every p is taken (finite inputs: rows past the last repeat it, keys past the
+    // sequence its last key), and only a chunk not wholly visible to the wave selects.
     float pr[2][4], ds[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const f32x4 lse4 = *reinterpret_cast<const f32x4*>(&L.lse[buf][16 * t + 4 * G]);
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&L.lse[buf][16 * t + 4 * G]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pr[t][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t][e], c, -l2[e]));
+    }
+    if (!(keys_in && rb >= r_vis_last && rb + RCH <= rows)) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = rb + 16 * t + 4 * G + e;
+          if (!(key_in && r < rows && r >= r_vis)) pr[t][e] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
       const f32x4 dd4 = *reinterpret_cast<const f32x4*>(&L.dd[buf][16 * t + 4 * G]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = rb + 16 * t + 4 * G + e;
-        const bool vis = key_in && r < rows && r >= r_vis;
-        pr[t][e] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t][e], c, -LOG2E * lse4[e])) : 0.f;
-        ds[t][e] = pr[t][e] * (pv[t][e] - dd4[e]);
-      }
+      for (int e = 0; e < 4; ++e) ds[t][e] = pr[t][e] * (pv[t][e] - dd4[e]);
     }
     const bf16x8 pb = {(__bf16)pr[0][0], (__bf16)pr[0][1], (__bf16)pr[0][2], (__bf16)pr[0][3],
                        (__bf16)pr[1][0], (__bf16)pr[1][1], (__bf16)pr[1][2], (__bf16)pr[1][3]};

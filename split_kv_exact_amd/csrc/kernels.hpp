@@ -69,6 +69,7 @@ struct BwdArgs {
   float* dv;
   float* ws_dq;      // per (block, KV head) dQ parts [partial_rows, D]
   float* ws_d;       // D_i = <dO_i, O_i> [total_q * Hq]
+  float* ws_l2;      // LSE_i * log2(e) [total_q * Hq], right after ws_d
   const SeqRec* seqs;
   int32_t S;
   const JobRec* jobs;

@@ -128,7 +128,10 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   pl->total_q = q_base;
   pl->partial_rows = row_base;
   pl->ws_lse_offset = align16(uint64_t(row_base) * pl->D * sizeof(float));
-  pl->ws_bytes = pl->ws_lse_offset + align16(uint64_t(row_base) * sizeof(float));
+  // The LSE area also holds the backward pass's two per-row values (D and the LSE in
+  // base 2), 2 * sum_s q_s * Hq floats, more than the partial rows of one-block sequences.
+  pl->ws_bytes = pl->ws_lse_offset +
+                 align16(std::max<uint64_t>(uint64_t(row_base), 2 * uint64_t(q_base) * uint64_t(pl->Hq)) * sizeof(float));
 
   // Units in enumeration order, with their costs.
   pl->u_seq.clear();
