@@ -211,6 +211,19 @@ def test_plan_info_sizes():
     assert inf["plan_bytes"] > 0 and inf["plan_bytes"] % 16 == 0
 
 
+def test_workspace_holds_the_backward_row_values():
+    """The backward pass keeps two floats per (query token, query head) in the LSE area
+    (D and the LSE in base 2). With one block per sequence the partial rows are exactly
+    sum q * Hq, half of that: the workspace grows to hold both."""
+    pl = splitkv_plan([50, 64], [7, 3], 8, 2, 128, 64, 8)  # one block each
+    inf = pl.info()
+    qh = 10 * 8
+    assert inf["partial_rows"] == qh
+    assert inf["workspace_bytes"] >= inf["ws_lse_offset"] + 2 * qh * 4
+    many = splitkv_plan([640, 320], [7, 3], 8, 2, 128, 64, 8).info()  # 10 and 5 blocks
+    assert many["workspace_bytes"] == many["ws_lse_offset"] + 4 * many["partial_rows"]
+
+
 @pytest.mark.parametrize("q, g, jobs, partial", [
     ([3, 1], 2, False, 0),          # every job below 8 row tiles: no matrix-path launch
     ([64, 125, 20], 4, True, 0),    # 256 and 500 rows: passes of 16 tiles only
