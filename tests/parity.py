@@ -82,7 +82,7 @@ def scale_of(wl):
 
 def oracle_threads() -> int:
     """Host threads for the oracle: the CPUs this process may use, capped by
-    OMP_NUM_THREADS where the environment sets it (16 on a one-GPU machine)."""
+    OMP_NUM_THREADS where the environment sets it."""
     import os
 
     avail = len(os.sched_getaffinity(0))
