@@ -129,11 +129,13 @@ splitkv::MergeArgs merge_args(const splitkv_plan_t* pl, const void* dev_plan, co
   if (multi_only) {
     m.seq_ids = reinterpret_cast<const int32_t*>(base + pl->layout.merge_multi);
     m.row_base = reinterpret_cast<const int64_t*>(base + pl->layout.merge_multi_base);
+    m.groups = reinterpret_cast<const splitkv::MergeGroup*>(base + pl->layout.merge_groups_multi);
     m.count = pl->num_multi;
     m.total_rows = pl->merge_rows_multi;
   } else {
     m.seq_ids = nullptr;
     m.row_base = reinterpret_cast<const int64_t*>(base + pl->layout.merge_all);
+    m.groups = reinterpret_cast<const splitkv::MergeGroup*>(base + pl->layout.merge_groups_all);
     m.count = pl->S;
     m.total_rows = pl->merge_rows_all;
   }
@@ -353,6 +355,7 @@ int splitkv_attn_backward(const splitkv_plan_t* pl, const void* dev_plan, const 
   b.total_q = pl->total_q;
   b.seq_ids = reinterpret_cast<const int32_t*>(base + pl->layout.merge_multi);
   b.row_base = reinterpret_cast<const int64_t*>(base + pl->layout.merge_multi_base);
+  b.groups = reinterpret_cast<const splitkv::MergeGroup*>(base + pl->layout.merge_groups_multi);
   b.count = pl->num_multi;
   b.total_rows = pl->merge_rows_multi;
   int64_t tiles = 0;

@@ -306,18 +306,19 @@ __global__ __launch_bounds__(W * 64, 2) void dq_kernel(BwdArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) void dqsum_kernel(BwdArgs a) {
   constexpr int DPL = D / 64;
+  static_assert(kMergeRowsPerGroup == 4, "four rows per workgroup, as the merge");
   const int64_t gw = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (gw >= a.total_rows) return;
   const int lane = threadIdx.x & 63;
-  int lo = 0, hi = a.count - 1;  // sequence with row_base[lo] <= gw < row_base[lo + 1]
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.row_base[mid] <= gw)
-      lo = mid;
-    else
-      hi = mid - 1;
+  // Sequence with row_base[lo] <= gw < row_base[lo + 1], as the merge finds it.
+  const MergeGroup e = a.groups[blockIdx.x];
+  int lo = e.lo_cross & ~kMergeCross;
+  int sid = e.seq;
+  if (e.lo_cross & kMergeCross) {
+    while (lo + 1 < a.count && a.row_base[lo + 1] <= gw) ++lo;
+    sid = a.seq_ids[lo];
   }
-  const SeqRec sq = a.seqs[a.seq_ids[lo]];
+  const SeqRec sq = a.seqs[sid];
   const int64_t rem = gw - a.row_base[lo];
   const int kv = int(rem / sq.rows);
   const int r = int(rem - int64_t(kv) * sq.rows);

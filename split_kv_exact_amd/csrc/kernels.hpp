@@ -44,6 +44,7 @@ struct MergeArgs {
   const SeqRec* seqs;
   const int32_t* seq_ids;    // sequences to merge (null: all sequences 0..count-1)
   const int64_t* row_base;   // prefix over those sequences of Hkv * rows
+  const MergeGroup* groups;  // per workgroup: the sequence of its first row
   int32_t count;             // number of sequences to merge
   int64_t total_rows;        // row_base[count]
   int32_t Hq, Hkv, g;
@@ -79,6 +80,7 @@ struct BwdArgs {
   // Summing the dQ parts of multi-block sequences (the merge's row mapping).
   const int32_t* seq_ids;
   const int64_t* row_base;
+  const MergeGroup* groups;
   int32_t count;
   int64_t total_rows;
   int64_t key_tiles;  // sum over sequences of ceil(n_s / 64)

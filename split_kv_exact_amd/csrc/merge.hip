@@ -6,6 +6,9 @@
 //   LSE = M + ln sum_b w_b,
 // because e^(LSE_b) O_b and e^(LSE_b) are the block's sums of e^s v and e^s.
 //
+// A workgroup merges kMergeRowsPerGroup consecutive rows; the plan image names the
+// sequence of its first row, so a row's sequence costs one load (a group that straddles
+// two sequences walks on from there).
 // Layout of the work: lane b holds LSE_b (64 blocks at a time), so M and sum_b w_b are
 // wave reductions; the output row is then accumulated in block order, each lane owning
 // head_dim/64 dimensions, with the loads of 16 blocks issued before they are used (the
@@ -24,7 +27,7 @@ namespace {
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.69314718055994531f;
 constexpr float NEG_INF = -__builtin_huge_valf();
-constexpr int WAVES = 4;
+constexpr int WAVES = kMergeRowsPerGroup;
 constexpr int UNROLL = 16;
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -44,16 +47,15 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int64_t gw = int64_t(blockIdx.x) * WAVES + (threadIdx.x >> 6);
   if (gw >= a.total_rows) return;
   const int lane = threadIdx.x & 63;
-  // Sequence j with row_base[j] <= gw < row_base[j + 1]: row_base is non-decreasing, so
-  // the entries <= gw form a prefix; lanes test 64 entries per load.
-  int lo = 0;
-  for (int c0 = 0; c0 < a.count; c0 += 64) {
-    const int j = c0 + lane;
-    const uint64_t le = __ballot(j < a.count && a.row_base[j] <= gw);
-    if (le) lo = c0 + 63 - __builtin_clzll(le);
-    if (le != ~uint64_t(0)) break;
+  // Sequence lo with row_base[lo] <= gw < row_base[lo + 1]: the plan names the one of
+  // the workgroup's first row; only a group that straddles sequences looks further.
+  const MergeGroup e = a.groups[blockIdx.x];
+  int lo = e.lo_cross & ~kMergeCross;
+  int s = e.seq;
+  if (e.lo_cross & kMergeCross) {
+    while (lo + 1 < a.count && a.row_base[lo + 1] <= gw) ++lo;
+    s = a.seq_ids ? a.seq_ids[lo] : lo;
   }
-  const int s = a.seq_ids ? a.seq_ids[lo] : lo;
   const SeqRec sq = a.seqs[s];
   const int64_t rem = gw - a.row_base[lo];
   const int kv = int(rem / sq.rows);

@@ -246,6 +246,12 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   off = align16(off + sizeof(int32_t) * uint64_t(std::max(pl->num_multi, 1)));
   L.merge_multi_base = off;
   off = align16(off + sizeof(int64_t) * uint64_t(pl->num_multi + 1));
+  const int64_t groups_all = (pl->merge_rows_all + kMergeRowsPerGroup - 1) / kMergeRowsPerGroup;
+  const int64_t groups_multi = (pl->merge_rows_multi + kMergeRowsPerGroup - 1) / kMergeRowsPerGroup;
+  L.merge_groups_all = off;
+  off = align16(off + sizeof(MergeGroup) * uint64_t(std::max<int64_t>(groups_all, 1)));
+  L.merge_groups_multi = off;
+  off = align16(off + sizeof(MergeGroup) * uint64_t(std::max<int64_t>(groups_multi, 1)));
 
   // Jobs of the bf16 kernel in LPT order (units by cost descending, ties in
   // enumeration order); a unit expands to its KV heads, each head to its row passes.
@@ -571,6 +577,21 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
       ++j;
     }
   }
+  // Merge workgroups' sequences (every sequence has at least one row, so the prefixes
+  // rise strictly and a row's sequence is unique).
+  auto fill_groups = [&](MergeGroup* out, const int64_t* prefix, const int32_t* ids, int32_t count, int64_t total) {
+    int32_t lo = 0;
+    for (int64_t g0 = 0; g0 < total; g0 += kMergeRowsPerGroup) {
+      while (prefix[lo + 1] <= g0) ++lo;
+      const int64_t last = std::min<int64_t>(g0 + kMergeRowsPerGroup, total) - 1;
+      MergeGroup& e = out[g0 / kMergeRowsPerGroup];
+      e.lo_cross = lo | (last >= prefix[lo + 1] ? kMergeCross : 0);
+      e.seq = ids ? ids[lo] : lo;
+    }
+    (void)count;
+  };
+  fill_groups(reinterpret_cast<MergeGroup*>(base + L.merge_groups_all), ma, nullptr, S, pl->merge_rows_all);
+  fill_groups(reinterpret_cast<MergeGroup*>(base + L.merge_groups_multi), mb, mm, pl->num_multi, pl->merge_rows_multi);
   if (!jobs.empty()) std::memcpy(base + L.jobs, jobs.data(), sizeof(JobRec) * jobs.size());
   if (!wjobs.empty()) std::memcpy(base + L.wjobs, wjobs.data(), sizeof(int32_t) * wjobs.size());
   std::memcpy(base + L.job_ptr, job_ptr.data(), sizeof(int32_t) * (m + 1));

@@ -40,6 +40,20 @@ constexpr int32_t kPassTiles = 16;
 // Passes of at least this many row tiles run on the matrix path (partial_mma.hip).
 constexpr int32_t kMmaMinTiles = 8;
 
+// Merged rows per merge workgroup (one wavefront each).
+constexpr int32_t kMergeRowsPerGroup = 4;
+
+// Where a merge workgroup's rows are: the index lo, in the merged sequence list, of the
+// sequence holding the group's first row (row_base[lo] <= row < row_base[lo + 1]), with
+// bit 31 set when a later row of the group lies in a later sequence, and that sequence's
+// id s. One entry per workgroup, so a row finds its sequence in one load.
+struct MergeGroup {
+  int32_t lo_cross;
+  int32_t seq;
+};
+static_assert(sizeof(MergeGroup) == 8, "MergeGroup layout");
+constexpr int32_t kMergeCross = int32_t(0x80000000u);
+
 // The plan's scheduling area: kQueues uint32 counters of the shared tail's
 // sub-queues (the next entry of each; one per 64-byte line, so that workgroups on
 // different sub-queues do not contend), then the count of finished workgroups. Zero
@@ -81,6 +95,8 @@ struct ImageLayout {
   uint64_t merge_all;   // int64[S + 1]: prefix of Hkv * rows over all sequences
   uint64_t merge_multi; // int32[S_multi] sequence ids with nb > 1, then
   uint64_t merge_multi_base;  // int64[S_multi + 1]: prefix of Hkv * rows over them
+  uint64_t merge_groups_all;   // MergeGroup[ceil(rows / kMergeRowsPerGroup)] over all sequences
+  uint64_t merge_groups_multi; // the same over the sequences with nb > 1
   uint64_t jobs;        // JobRec[num_jobs] in LPT order
   uint64_t wjobs;       // int32[num_jobs]: job indices of each workgroup's units, workgroup by workgroup
   uint64_t job_ptr;     // int32[m + 1]: workgroup w's jobs are wjobs[job_ptr[w] .. job_ptr[w+1])
