@@ -358,9 +358,8 @@ int splitkv_attn_backward(const splitkv_plan_t* pl, const void* dev_plan, const 
   b.groups = reinterpret_cast<const splitkv::MergeGroup*>(base + pl->layout.merge_groups_multi);
   b.count = pl->num_multi;
   b.total_rows = pl->merge_rows_multi;
-  int64_t tiles = 0;
-  for (const splitkv::SeqRec& r : pl->seqs) tiles += (r.n + 63) / 64;
-  b.key_tiles = tiles;
+  b.key_tiles = pl->num_key_tiles;
+  b.tiles = reinterpret_cast<const splitkv::KeyTile*>(base + pl->layout.key_tiles);
   b.dq_waves = pl->max_rows <= 128 ? 4 : 8;
   return hip_status(splitkv::launch_backward_bf16(b, pl->D, static_cast<hipStream_t>(hip_stream)),
                     "backward launch");

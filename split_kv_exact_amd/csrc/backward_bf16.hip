@@ -361,18 +361,14 @@ __global__ __launch_bounds__(256, 3) void dkv_kernel(BwdArgs a) {
   const int G = lane >> 4, li = lane & 15;
   const float c = a.scale * LOG2E;
 
-  // Workgroup -> (sequence s, KV head kv, 64-key tile t).
+  // Workgroup -> (KV head kv, key tile): the plan image names the tile's sequence and
+  // its index there.
+  static_assert(kDkvTileKeys == 16 * KV_WAVES, "16 keys per wave");
   const int64_t wg = blockIdx.x;
   const int kv = int(wg % a.Hkv);
-  int64_t tile = wg / a.Hkv;
-  int s = 0;
-  for (;; ++s) {
-    const int64_t nt_s = (a.seqs[s].n + 63) / 64;
-    if (tile < nt_s || s + 1 == a.S) break;
-    tile -= nt_s;
-  }
-  const SeqRec sq = a.seqs[s];
-  const int64_t n = sq.n, k0 = tile * 64;
+  const KeyTile where = a.tiles[wg / a.Hkv];
+  const SeqRec sq = a.seqs[where.seq];
+  const int64_t n = sq.n, k0 = int64_t(where.tile) * kDkvTileKeys;
   const int rows = sq.rows;  // q * g
   // This lane's key (the wave's 16 keys) and its K and V rows as B operands
   // (lane: key li, dims 8 G + 32 dc).

@@ -83,7 +83,8 @@ struct BwdArgs {
   const MergeGroup* groups;
   int32_t count;
   int64_t total_rows;
-  int64_t key_tiles;  // sum over sequences of ceil(n_s / 64)
+  int64_t key_tiles;  // sum over sequences of ceil(n_s / kDkvTileKeys)
+  const KeyTile* tiles;  // where each key tile lies
   int32_t dq_waves;   // waves per dQ workgroup: 4 when every pass has at most 8 row tiles, else 8
 };
 

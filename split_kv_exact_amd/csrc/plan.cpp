@@ -61,9 +61,10 @@ bool validate_problem(const splitkv_problem* p, std::string* why) {
   if (total > 4.0e18) return fail("total unit cost beyond 2^62");
   // Block, unit, job and token indices are int32 in the plan records and the kernels:
   // the block count of a sequence, the number of units and the number of jobs (a unit
-  // per KV head and pass of up to kPassTiles row tiles) must fit.
+  // per KV head and pass of up to kPassTiles row tiles) must fit, and so must the number
+  // of kDkvTileKeys-key tiles the backward pass numbers.
   const int64_t imax = INT32_MAX;
-  int64_t units = 0, jobs = 0;
+  int64_t units = 0, jobs = 0, key_tiles = 0;
   for (int32_t s = 0; s < p->batch; ++s) {
     const int64_t nb = (p->kv_lens[s] + p->block_len - 1) / p->block_len;
     if (nb > imax) return fail("a sequence has more than 2^31 - 1 blocks");
@@ -72,7 +73,9 @@ bool validate_problem(const splitkv_problem* p, std::string* why) {
     const int64_t per_block = p->granularity == SPLITKV_UNIT_SEQ_BLOCK_KVHEAD ? p->num_kv_heads : 1;
     units += nb * per_block;
     jobs += nb * p->num_kv_heads * passes;
+    key_tiles += (p->kv_lens[s] + kDkvTileKeys - 1) / kDkvTileKeys;
     if (units > imax || jobs > imax) return fail("more than 2^31 - 1 units or jobs");
+    if (key_tiles > imax) return fail("more than 2^31 - 1 key tiles of the backward pass");
   }
   return true;
 }
@@ -252,6 +255,10 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   off = align16(off + sizeof(MergeGroup) * uint64_t(std::max<int64_t>(groups_all, 1)));
   L.merge_groups_multi = off;
   off = align16(off + sizeof(MergeGroup) * uint64_t(std::max<int64_t>(groups_multi, 1)));
+  pl->num_key_tiles = 0;
+  for (int32_t s = 0; s < S; ++s) pl->num_key_tiles += (pl->seqs[s].n + kDkvTileKeys - 1) / kDkvTileKeys;
+  L.key_tiles = off;
+  off = align16(off + sizeof(KeyTile) * uint64_t(std::max<int64_t>(pl->num_key_tiles, 1)));
 
   // Jobs of the bf16 kernel in LPT order (units by cost descending, ties in
   // enumeration order); a unit expands to its KV heads, each head to its row passes.
@@ -591,6 +598,14 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
     (void)count;
   };
   fill_groups(reinterpret_cast<MergeGroup*>(base + L.merge_groups_all), ma, nullptr, S, pl->merge_rows_all);
+  KeyTile* kt = reinterpret_cast<KeyTile*>(base + L.key_tiles);
+  for (int32_t s = 0; s < S; ++s) {
+    const int64_t nt = (pl->seqs[s].n + kDkvTileKeys - 1) / kDkvTileKeys;
+    for (int64_t t = 0; t < nt; ++t, ++kt) {
+      kt->seq = s;
+      kt->tile = int32_t(t);
+    }
+  }
   fill_groups(reinterpret_cast<MergeGroup*>(base + L.merge_groups_multi), mb, mm, pl->num_multi, pl->merge_rows_multi);
   if (!jobs.empty()) std::memcpy(base + L.jobs, jobs.data(), sizeof(JobRec) * jobs.size());
   if (!wjobs.empty()) std::memcpy(base + L.wjobs, wjobs.data(), sizeof(int32_t) * wjobs.size());

@@ -54,6 +54,15 @@ struct MergeGroup {
 static_assert(sizeof(MergeGroup) == 8, "MergeGroup layout");
 constexpr int32_t kMergeCross = int32_t(0x80000000u);
 
+// Keys per workgroup of the backward dK/dV kernel, and each such key tile's place: the
+// sequence and the tile's index within it (tiles numbered sequence by sequence).
+constexpr int32_t kDkvTileKeys = 64;
+struct KeyTile {
+  int32_t seq;
+  int32_t tile;
+};
+static_assert(sizeof(KeyTile) == 8, "KeyTile layout");
+
 // The plan's scheduling area: kQueues uint32 counters of the shared tail's
 // sub-queues (the next entry of each; one per 64-byte line, so that workgroups on
 // different sub-queues do not contend), then the count of finished workgroups. Zero
@@ -97,6 +106,7 @@ struct ImageLayout {
   uint64_t merge_multi_base;  // int64[S_multi + 1]: prefix of Hkv * rows over them
   uint64_t merge_groups_all;   // MergeGroup[ceil(rows / kMergeRowsPerGroup)] over all sequences
   uint64_t merge_groups_multi; // the same over the sequences with nb > 1
+  uint64_t key_tiles;   // KeyTile[num_key_tiles]: the backward dK/dV kernel's key tiles
   uint64_t jobs;        // JobRec[num_jobs] in LPT order
   uint64_t wjobs;       // int32[num_jobs]: job indices of each workgroup's units, workgroup by workgroup
   uint64_t job_ptr;     // int32[m + 1]: workgroup w's jobs are wjobs[job_ptr[w] .. job_ptr[w+1])
