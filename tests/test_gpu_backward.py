@@ -54,6 +54,10 @@ CASES = [
     # one query token's rows).
     _wl("group_of_3", [900, 300, 41], [7, 3, 2], 6, 2, 128, 256, 5),
     _wl("group_of_64", [500, 130], [3, 2], 64, 1, 64, 128, 4),
+    # Many short sequences: 64-key tiles of 160 sequences found through the plan's tile
+    # table, and dQ sums whose four-row groups straddle sequences.
+    _wl("many_short_sequences", [(37 * i) % 400 + 1 for i in range(160)],
+        [min((37 * i) % 400 + 1, 1 + i % 4) for i in range(160)], 6, 2, 128, 64, 32),
 ]
 
 

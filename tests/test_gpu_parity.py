@@ -36,6 +36,9 @@ def _wl(name, kv, q, hq, hkv, d, b, m, dtype="bfloat16", causal=True, gran=0, se
                     boost=8.0, granularity=gran)
 
 
+MANY_KV = [(37 * i) % 400 + 1 for i in range(240)]
+MANY_Q = [min(n, 1 + i % 4) for i, n in enumerate(MANY_KV)]
+
 SMALL = [
     get_workload("small"),
     _wl("ragged_bf16_d128", [1000, 333, 77, 2100, 16], [16, 5, 1, 40, 16], 32, 8, 128, 256, 16),
@@ -66,6 +69,10 @@ SMALL = [
     # A GQA group that is not a power of two (g = 3) and one of 64 heads per KV head.
     _wl("group_of_3", [900, 300, 41], [7, 3, 2], 6, 2, 128, 256, 5),
     _wl("group_of_64", [500, 130], [3, 2], 64, 1, 64, 128, 4),
+    # Many short sequences, one to seven 64-key blocks, 6 to 24 rows per sequence: merge
+    # workgroups (four rows) often straddle two sequences, in both the merge of every
+    # sequence and the fused call's merge of the multi-block ones.
+    _wl("many_short_sequences", MANY_KV, MANY_Q, 6, 2, 128, 64, 32),
 ]
 # Matrix-path kernel variant each case must run (mma_partial_passes of the plan info).
 MMA_PARTIAL_PASSES = {"full_passes_d128": 0, "full_passes_d64": 0, "full_passes_q_equals_n": 0,
