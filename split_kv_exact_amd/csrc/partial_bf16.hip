@@ -37,16 +37,19 @@
 //     wave stores whole tiles.
 //   * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16, A = 16
 //     keys x 32 dims from the K tile, B = 32 dims x 16 rows of Q in registers). A lane
-//     then owns one query row and 4 keys per 16-key tile: the row max needs two
-//     cross-lane steps and the row sum none until the end of the job.
+//     then owns one query row and 4 keys per 16-key tile: the row sum needs no
+//     cross-lane step until the end of the job.
 //   * Output is accumulated transposed, O^T += V^T P^T. P^T comes straight from the
 //     score registers (rounded to bf16); V^T is read with ds_read_b64_tr_b16, which
 //     hands each lane four keys of one dimension. Pairs of 16-key tiles feed
 //     v_mfma_f32_16x16x32_bf16; the key order inside the contraction is permuted
 //     identically on both operands, which leaves the sum unchanged.
 //   * Softmax runs in base 2 on raw scores: p = 2^(s*c - m*c), c = scale*log2(e), m a
-//     running reference max. The LSE uses the sum of the fp32 p (LSE = scale*m + ln l);
-//     O is normalised by the sum of the bf16-rounded p it was accumulated from.
+//     running reference max that moves only when a row's scores rise more than 2^8 in
+//     p above it. p is taken first; the row max is formed (two cross-lane steps) only
+//     when a lane's sum of p exceeds 2^7. The LSE uses the sum of the fp32 p (LSE =
+//     scale*m + ln l); O is normalised by the sum of the bf16-rounded p it was
+//     accumulated from.
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"

@@ -27,7 +27,8 @@
 //     also waits for the stage DMA issued before them, once per job).
 //   * The arithmetic is that of the other kernel: S^T = K Q^T (v_mfma_f32_16x16x32_bf16,
 //     a lane owns one query row and four keys per 16-key tile), online softmax in base 2
-//     with a thresholded reference max, p rounded to bf16 for O^T += V^T P^T (V^T read
+//     with a thresholded reference max (p first, the row max only when a lane's sum of
+//     p says the reference may move), p rounded to bf16 for O^T += V^T P^T (V^T read
 //     with ds_read_b64_tr_b16), O normalised by the MFMA sum of the rounded p, the LSE
 //     from the fp32 sum of p. Both kernels give the same result for a job bit for bit.
 #include <hip/hip_runtime.h>
