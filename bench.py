@@ -230,7 +230,11 @@ def measure(skv, M, wl, q, k, v, args, dev, stream, xcd=True, flush=None):
         plan_times.append((time.perf_counter_ns() - t0) / 1e6)
     plan_times.sort()
     info = plan.info()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter_ns()
     dev_plan = skv.splitkv_plan_upload(plan, dev)
+    torch.cuda.synchronize()
+    upload_ms = (time.perf_counter_ns() - t0) / 1e6
     ws = skv.workspace(plan, dev)
     out = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
     lse = torch.empty((wl.total_q, wl.num_q_heads), dtype=torch.float32, device=dev)
@@ -352,6 +356,8 @@ def measure(skv, M, wl, q, k, v, args, dev, stream, xcd=True, flush=None):
             "makespan": info["makespan"],
             "lower_bound": info["lower_bound"],
             "plan_ms_median": round(plan_times[len(plan_times) // 2], 4),
+            "plan_upload_ms": round(upload_ms, 4),
+            "plan_bytes": int(info["plan_bytes"]),
             "schedule": sched,
             "schedule_run": ran,
             "executed": {
