@@ -5,7 +5,7 @@ One step = one fused ``splitkv_attn`` call (partial attention of every LPT unit,
 then the log-sum-exp merge) over the whole workload, inputs resident in HBM.
 Prints one JSON line. Default workload: the largest one that fits one GPU, the mixed
 batch of 128 decode sequences (1 query, contexts 8K-128K) and 4 prefill chunks (2048
-queries over 64K contexts), GQA 64/8, head_dim 128, KV block 4096, 256 workers (bf16);
+queries over 64K contexts), GQA 64/8, head_dim 128, KV block 8192, 256 workers (bf16);
 the decode-only part of that batch and the 8-sequence batch (the memory-bound shapes)
 are timed after it and reported under "sub_runs". Every timed step starts from cold
 caches (a 1 GiB write before it, outside its events).
@@ -52,15 +52,16 @@ def _kernel_sha(csrc: str | None = None) -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(wl_key: str):
+def _traffic(wl_key: str, wl_name: str):
     """HBM bytes per partial-attention launch from committed rocprofv3 counter runs, if
-    they were taken on the current kernel sources; otherwise None."""
+    they were taken on the current kernel sources and on this workload (its name holds
+    its shape and block size); otherwise None."""
     p = os.path.join(ROOT, "profiles", f"traffic_{wl_key}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("kernel_sha") != _kernel_sha():
+    if t.get("kernel_sha") != _kernel_sha() or t.get("workload") != wl_name:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -338,7 +339,7 @@ def measure(skv, M, wl, q, k, v, args, dev, stream, xcd=True, flush=None):
             "peak": peak,
             "unit": unit,
             "frac": round(achieved / peak, 4),
-            "traffic": _traffic(_wl_key(wl)),
+            "traffic": _traffic(_wl_key(wl), wl.name),
             "ms_per_launch": round(ms_partial, 5),
             "algorithmic_bytes_per_launch": eb,
             "algorithmic_flops_per_launch": fl,

@@ -34,6 +34,23 @@ def test_source_hash_ignores_comments_only(tmp_path):
     assert bench._kernel_sha(str(tmp_path)) != base
 
 
+def test_traffic_record_needs_current_sources_and_the_same_workload(tmp_path, monkeypatch):
+    """A committed counter record is used only on the sources and the workload (shape and
+    block size, both in the name) it was taken on."""
+    import json
+
+    (tmp_path / "profiles").mkdir()
+    rec = {"kernel_sha": "abc", "workload": "mix_b8192", "hbm_bytes_per_launch": 123}
+    (tmp_path / "profiles" / "traffic_mix.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "_kernel_sha", lambda csrc=None: "abc")
+    assert bench._traffic("mix", "mix_b8192") == 123
+    assert bench._traffic("mix", "mix_b4096") is None
+    assert bench._traffic("other", "mix_b8192") is None
+    monkeypatch.setattr(bench, "_kernel_sha", lambda csrc=None: "def")
+    assert bench._traffic("mix", "mix_b8192") is None
+
+
 def test_byte_and_flop_accounting_by_hand():
     # Two causal sequences, bf16, Hq = 4, Hkv = 2 (g = 2), D = 8, B = 4.
     wl = Workload(name="t", dtype="bfloat16", kv_lens=(6, 3), q_lens=(2, 3), num_q_heads=4, num_kv_heads=2,

@@ -191,21 +191,23 @@ def _mixed_decode_lens(seed: int) -> np.ndarray:
 def mixed_decode_prefill_bf16(seed: int = 1005) -> Workload:
     """bf16 mixed batch: 128 decode sequences (1 query, context uniform in [8192,
     131072]) followed by 4 prefill chunks (the last 2048 tokens of 65536-token
-    contexts, causal on the chunk). GQA 64/8, head_dim 128. Readings: KV block 4096
-    (the shape gives none); 0.1% of (token, kv-head) key rows, drawn Bernoulli, are
-    multiplied by 8 before the bf16 cast (a power of two, so the cast stays exact)."""
+    contexts, causal on the chunk). GQA 64/8, head_dim 128. Readings: KV block 8192
+    (the shape gives none: the largest block that still gives every worker a prefill
+    unit, so the fewest partials for the exact merge); 0.1% of (token, kv-head) key
+    rows, drawn Bernoulli, are multiplied by 8 before the bf16 cast (a power of two, so
+    the cast stays exact)."""
     n_dec = _mixed_decode_lens(seed)
     kv = tuple(int(x) for x in n_dec) + (65536,) * 4
     q = (1,) * 128 + (2048,) * 4
     return Workload(
-        name="mixed_bf16_128dec-ctx8k-128k_4prefill-2048of64k_gqa64-8_d128_b4096",
+        name="mixed_bf16_128dec-ctx8k-128k_4prefill-2048of64k_gqa64-8_d128_b8192",
         dtype="bfloat16",
         kv_lens=kv,
         q_lens=q,
         num_q_heads=64,
         num_kv_heads=8,
         head_dim=128,
-        block_len=4096,
+        block_len=8192,
         num_workers=256,
         seed=seed,
         boost_frac=0.001,
@@ -215,18 +217,18 @@ def mixed_decode_prefill_bf16(seed: int = 1005) -> Workload:
 
 def decode_only_bf16(seed: int = 1005) -> Workload:
     """The 128 decode sequences of the mixed batch on their own: same seed, same
-    context lengths and the same tensor recipe (boosted keys included), without the
+    context lengths, KV block and tensor recipe (boosted keys included), without the
     prefill chunks. This is the memory-bound part of that batch."""
     n_dec = _mixed_decode_lens(seed)
     return Workload(
-        name="decode128_bf16_ctx8k-128k_q1_gqa64-8_d128_b4096",
+        name="decode128_bf16_ctx8k-128k_q1_gqa64-8_d128_b8192",
         dtype="bfloat16",
         kv_lens=tuple(int(x) for x in n_dec),
         q_lens=(1,) * 128,
         num_q_heads=64,
         num_kv_heads=8,
         head_dim=128,
-        block_len=4096,
+        block_len=8192,
         num_workers=256,
         seed=seed,
         boost_frac=0.001,
