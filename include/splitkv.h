@@ -33,13 +33,17 @@
  *   K,V [sum_s n_s, Hkv, D]  likewise with their own strides; d is contiguous
  *   out [sum_s q_s, Hq,  D]  fp32, contiguous
  *   lse [sum_s q_s, Hq]      fp32, natural log, contiguous
- *   Workspace (fp32): partial outputs first, then partial LSEs at byte offset
+ *   Workspace: partial outputs first, then partial LSEs at byte offset
  *   info.ws_lse_offset. The partial of unit (s, b, kv head k) for query row
  *   r = i*g + (h - k*g) (query token i, query head h) is row
  *       R = seq_row_base[s] + (k * nb_s + b) * (q_s * g) + r
  *   with nb_s = ceil(n_s / B), g = Hq / Hkv and seq_row_base[s] the sum over earlier
- *   sequences of nb_t * Hkv * q_t * g; its output is ws[R*D .. R*D + D) and its
- *   LSE is ws_lse[R].
+ *   sequences of nb_t * Hkv * q_t * g. With SPLITKV_PARTIAL_F32 its output is the fp32
+ *   ws[R*D .. R*D + D) and its LSE the fp32 ws_lse[R]. With SPLITKV_PARTIAL_F16_ROWSCALE
+ *   its output is the fp16 elements ws_h[R*D .. R*D + D) (ws_h = the workspace base as
+ *   fp16) times a row scale, and ws_lse holds the fp32 pair (LSE, scale) at [2R, 2R + 1];
+ *   the scale is the row's largest |O| (0 for a row without a visible key), so every
+ *   element is within scale * 2^-12 of the fp32 value.
  */
 #ifndef SPLITKV_H
 #define SPLITKV_H
@@ -52,7 +56,7 @@ extern "C" {
 #endif
 
 #define SPLITKV_VERSION_MAJOR 0
-#define SPLITKV_VERSION_MINOR 6
+#define SPLITKV_VERSION_MINOR 7
 
 typedef enum {
   SPLITKV_OK = 0,
@@ -94,6 +98,11 @@ typedef enum { SPLITKV_UNIT_SEQ_BLOCK_KVHEAD = 0, SPLITKV_UNIT_SEQ_BLOCK = 1 } s
  * runs). fp32 launches always use the static assignment. */
 typedef enum { SPLITKV_SCHED_AUTO = 0, SPLITKV_SCHED_QUEUE = 1, SPLITKV_SCHED_STATIC = 2 } splitkv_schedule;
 
+/* How the per-block partial outputs are stored in the workspace (layout above). The
+ * row-scaled fp16 form halves the bytes the partials move (written by the partial
+ * attention, read by the merge); bf16 inputs only. */
+typedef enum { SPLITKV_PARTIAL_F32 = 0, SPLITKV_PARTIAL_F16_ROWSCALE = 1 } splitkv_partial_format;
+
 /* Problem description. Host memory, caller-owned, read only during splitkv_plan. */
 typedef struct {
   int32_t batch;            /* S >= 1 sequences                                      */
@@ -116,6 +125,8 @@ typedef struct {
                              * the worker_clock of a calibration launch: the plan's    *
                              * most loaded workers are then placed on workgroups of    *
                              * the fastest XCDs. The plan itself is unchanged.         */
+  int32_t partial_format;   /* splitkv_partial_format; 0 (fp32 partials) is the only    *
+                             * choice for fp32 inputs                                  */
 } splitkv_problem;
 
 typedef struct splitkv_plan_s splitkv_plan_t; /* opaque, library-owned host object */
@@ -153,6 +164,7 @@ typedef struct {
                                      * tiles: that launch then runs the kernel variant   *
                                      * whose waves may skip their second row tile; 0     *
                                      * when every such job covers 16 (or there is none)  */
+  int32_t partial_format;           /* splitkv_partial_format of the plan               */
 } splitkv_plan_info;
 
 /* Device inputs. Pointers are device memory, caller-owned, read only. Strides are in
@@ -227,8 +239,8 @@ void splitkv_plan_destroy(splitkv_plan_t *plan);
  * every row is written, rows that see no key of a block get O = 0 and LSE = -inf.
  * dev_plan is the uploaded plan; the launch also uses its scheduling area.
  * Errors: INVALID_ARG (null/misaligned pointers, strides), UNSUPPORTED (no kernel for
- * dtype/head_dim, bf16 stride above 2^24), WORKSPACE (ws_bytes < workspace_bytes),
- * HIP (launch failed). */
+ * dtype/head_dim, bf16 stride above 2^24, fp32 inputs on a plan with fp16 partials),
+ * WORKSPACE (ws_bytes < workspace_bytes), HIP (launch failed). */
 int splitkv_partial_attn(const splitkv_plan_t *plan, void *dev_plan, const splitkv_inputs *in,
                          float *ws, size_t ws_bytes, void *hip_stream);
 
@@ -242,7 +254,9 @@ int splitkv_merge(const splitkv_plan_t *plan, const void *dev_plan, const float 
 
 /* Fused call: partial attention and merge enqueued back to back on hip_stream, with
  * sequences of a single block written straight to out/lse. Same arguments and errors
- * as the two calls above. */
+ * as the two calls above. Its output is the bits of the two calls' output, except that
+ * under SPLITKV_PARTIAL_F16_ROWSCALE the rows of single-block sequences skip the fp16
+ * rounding of the stored partial (the two then differ by at most the bound above). */
 int splitkv_attn(const splitkv_plan_t *plan, void *dev_plan, const splitkv_inputs *in,
                  float *ws, size_t ws_bytes, float *out, float *lse, void *hip_stream);
 

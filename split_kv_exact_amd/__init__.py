@@ -22,3 +22,4 @@ from .api import (  # noqa: F401
     workspace,
     workspace_views,
 )
+from ._lib import SPLITKV_PARTIAL_F16_ROWSCALE, SPLITKV_PARTIAL_F32  # noqa: F401

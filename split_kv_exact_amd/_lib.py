@@ -31,6 +31,9 @@ SPLITKV_SCHED_AUTO = 0
 SPLITKV_SCHED_QUEUE = 1
 SPLITKV_SCHED_STATIC = 2
 
+SPLITKV_PARTIAL_F32 = 0
+SPLITKV_PARTIAL_F16_ROWSCALE = 1
+
 # Every function include/splitkv.h declares.
 EXPORTED = (
     "splitkv_version",
@@ -63,6 +66,7 @@ class Problem(ctypes.Structure):
         ("granularity", ctypes.c_int32),
         ("cost_ridge_rows", ctypes.c_int32),
         ("xcd_speed", ctypes.POINTER(ctypes.c_int32)),
+        ("partial_format", ctypes.c_int32),
     ]
 
 
@@ -86,6 +90,7 @@ class PlanInfo(ctypes.Structure):
         ("auto_schedule", ctypes.c_int32),
         ("num_mma_jobs", ctypes.c_int64),
         ("mma_partial_passes", ctypes.c_int32),
+        ("partial_format", ctypes.c_int32),
     ]
 
 

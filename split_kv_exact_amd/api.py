@@ -87,11 +87,14 @@ def splitkv_plan(
     granularity: int = L.SPLITKV_UNIT_SEQ_BLOCK_KVHEAD,
     cost_ridge_rows: int = 0,
     xcd_speed: Sequence[int] | None = None,
+    partial_format: int = L.SPLITKV_PARTIAL_F32,
 ) -> Plan:
     """Build the LPT plan on the host (``splitkv_plan``). ``cost_ridge_rows`` selects the
     unit cost: 0 is q * len * heads, R > 0 is len * max(q * g, R) per KV head.
     ``xcd_speed`` (8 relative speeds, or None) places the most loaded workers on the
-    workgroups of the fastest XCDs."""
+    workgroups of the fastest XCDs. ``partial_format``: how the per-block partials are
+    stored (``SPLITKV_PARTIAL_F32``, or ``SPLITKV_PARTIAL_F16_ROWSCALE`` for bf16 inputs,
+    half the bytes)."""
     lib = L.load()
     kv = np.ascontiguousarray(np.asarray(kv_lens, dtype=np.int64))
     ql = np.ascontiguousarray(np.asarray(q_lens, dtype=np.int32))
@@ -107,6 +110,7 @@ def splitkv_plan(
         causal=int(bool(causal)),
         granularity=granularity,
         cost_ridge_rows=cost_ridge_rows,
+        partial_format=partial_format,
     )
     speeds = None
     if xcd_speed is not None:
@@ -119,14 +123,18 @@ def splitkv_plan(
     problem = dict(kv_lens=kv.tolist(), q_lens=ql.tolist(), num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                    head_dim=head_dim, block_len=block_len, num_workers=num_workers, causal=bool(causal),
                    granularity=granularity, cost_ridge_rows=cost_ridge_rows,
-                   xcd_speed=None if speeds is None else speeds.tolist())
+                   xcd_speed=None if speeds is None else speeds.tolist(), partial_format=partial_format)
     return Plan(h, problem, lib)
 
 
-def plan_for(wl, cost_ridge_rows: int = 0, xcd_speed: Sequence[int] | None = None) -> Plan:
-    """Plan for a ``workloads.Workload``."""
+def plan_for(wl, cost_ridge_rows: int = 0, xcd_speed: Sequence[int] | None = None,
+             partial_format: int | None = None) -> Plan:
+    """Plan for a ``workloads.Workload``; its partials are row-scaled fp16 for bf16
+    inputs and fp32 for fp32 inputs unless ``partial_format`` says otherwise."""
+    if partial_format is None:
+        partial_format = L.SPLITKV_PARTIAL_F16_ROWSCALE if wl.dtype == "bfloat16" else L.SPLITKV_PARTIAL_F32
     return splitkv_plan(wl.kv_lens, wl.q_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_len,
-                        wl.num_workers, wl.causal, wl.granularity, cost_ridge_rows, xcd_speed)
+                        wl.num_workers, wl.causal, wl.granularity, cost_ridge_rows, xcd_speed, partial_format)
 
 
 # --------------------------------------------------------------------------- device side
@@ -160,11 +168,18 @@ def workspace(plan: Plan, device=None):
 
 
 def workspace_views(plan: Plan, ws) -> Tuple[object, object]:
-    """(partial outputs [partial_rows, D], partial LSEs [partial_rows]) views of a workspace."""
+    """(partial outputs [partial_rows, D], partial LSEs [partial_rows]) of a workspace, as
+    fp32: views for fp32 partials; for row-scaled fp16 partials, new tensors holding each
+    element times its row's scale."""
+    torch = _torch()
     inf = plan.info()
     rows, d = int(inf["partial_rows"]), int(plan.problem["head_dim"])
     off = int(inf["ws_lse_offset"]) // 4
-    return ws[: rows * d].view(rows, d), ws[off: off + rows]
+    if int(inf["partial_format"]) == L.SPLITKV_PARTIAL_F32:
+        return ws[: rows * d].view(rows, d), ws[off: off + rows]
+    h = ws[: (rows * d + 1) // 2].view(torch.float16)[: rows * d].view(rows, d)
+    pairs = ws[off: off + 2 * rows].view(rows, 2)
+    return h.float() * pairs[:, 1:2], pairs[:, 0].clone()
 
 
 _SCHEDULES = {"auto": L.SPLITKV_SCHED_AUTO, "queue": L.SPLITKV_SCHED_QUEUE, "static": L.SPLITKV_SCHED_STATIC}

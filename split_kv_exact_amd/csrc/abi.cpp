@@ -35,6 +35,8 @@ int check_plan(const splitkv_plan_t* pl, const void* dev_plan) {
 int check_inputs(const splitkv_plan_t* pl, const splitkv_inputs* in, float* scale_out) {
   if (!in) return fail(SPLITKV_ERR_INVALID_ARG, "inputs is NULL");
   if (in->dtype != SPLITKV_F32 && in->dtype != SPLITKV_BF16) return fail(SPLITKV_ERR_INVALID_ARG, "unknown dtype");
+  if (in->dtype == SPLITKV_F32 && pl->pfmt == SPLITKV_PARTIAL_F16_ROWSCALE)
+    return fail(SPLITKV_ERR_UNSUPPORTED, "fp32 inputs need a plan with fp32 partials (partial_format 0)");
   if (pl->D != 64 && pl->D != 128)
     return fail(SPLITKV_ERR_UNSUPPORTED, "kernels exist for head_dim 64 and 128 only");
   if (!in->q || !in->k || !in->v) return fail(SPLITKV_ERR_INVALID_ARG, "q, k and v must be non-NULL");
@@ -116,6 +118,7 @@ splitkv::PartialArgs partial_args(const splitkv_plan_t* pl, void* dev_plan, cons
   a.causal = pl->causal;
   a.ws_o = ws;
   a.ws_lse = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + pl->ws_lse_offset);
+  a.h16 = pl->pfmt == SPLITKV_PARTIAL_F16_ROWSCALE ? 1 : 0;
   a.out = nullptr;
   a.lse = nullptr;
   return a;
@@ -144,6 +147,7 @@ splitkv::MergeArgs merge_args(const splitkv_plan_t* pl, const void* dev_plan, co
   m.g = pl->g;
   m.ws_o = ws;
   m.ws_lse = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(ws) + pl->ws_lse_offset);
+  m.h16 = pl->pfmt == SPLITKV_PARTIAL_F16_ROWSCALE ? 1 : 0;
   m.out = out;
   m.lse = lse;
   return m;
@@ -213,6 +217,7 @@ int splitkv_plan_info_get(const splitkv_plan_t* pl, splitkv_plan_info* info) {
   info->auto_schedule = pl->queue_default && pl->tail_start < pl->num_jobs ? SPLITKV_SCHED_QUEUE : SPLITKV_SCHED_STATIC;
   info->num_mma_jobs = pl->num_mma_jobs;
   info->mma_partial_passes = pl->num_mma_jobs > 0 && pl->mma_partial_passes ? 1 : 0;
+  info->partial_format = pl->pfmt;
   return SPLITKV_OK;
 }
 

@@ -31,12 +31,15 @@ struct PartialArgs {
   int32_t clock_add;        // bf16 kernel: an earlier launch wrote the clocks; add its busy time
   int32_t num_workers;
   int32_t Hq, Hkv, g, B, causal;
-  float* ws_o;    // partial outputs [partial_rows, D]
-  float* ws_lse;  // partial LSEs [partial_rows]
+  float* ws_o;    // partial outputs [partial_rows, D] (fp32; fp16 elements when h16)
+  float* ws_lse;  // partial LSEs [partial_rows] (fp32; (LSE, row scale) pairs when h16)
   // When non-null, sequences with a single block write their final result here
   // instead of the workspace (the fused path).
   float* out;
   float* lse;
+  // Partials stored as fp16 elements times a per-row fp32 scale. Read on the host only:
+  // the launch picks the kernel variant.
+  int32_t h16;
 };
 
 // Arguments of the merge kernel (one wavefront per merged row).
@@ -49,8 +52,9 @@ struct MergeArgs {
   int64_t total_rows;        // row_base[count]
   int32_t Hq, Hkv, g;
   float scale;
-  const float* ws_o;
-  const float* ws_lse;
+  const float* ws_o;    // fp32 partial outputs, or fp16 elements when h16
+  const float* ws_lse;  // fp32 LSEs, or (LSE, row scale) pairs when h16
+  int32_t h16;
   float* out;
   float* lse;
 };

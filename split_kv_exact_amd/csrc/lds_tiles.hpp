@@ -1,4 +1,5 @@
-// LDS tile helpers shared by the bf16 attention kernels (gfx950).
+// LDS tile helpers and the partial-output store shared by the bf16 attention kernels
+// (gfx950).
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -10,6 +11,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) const bf16x8* lds_bf16x8;
 
@@ -21,6 +24,34 @@ template <int CH>
 __device__ __forceinline__ int swz_row(int row, int c) { return c ^ (row & (CH - 1)); }
 template <int CH>
 __device__ __forceinline__ int swz_tr(int row, int c) { return c ^ ((2 * row) & (CH - 1)); }
+
+// Row-scaled fp16 store of one row of a partial output. o[dt] holds this lane's
+// elements of the row, dims 16 dt + 4 G .. + 3 (the transposed accumulator of both
+// bf16 kernels; the row's other elements are on the lanes 16 and 32 apart), before
+// normalisation by inv. The row's scale is its largest |o * inv|; each element is
+// stored as fp16(o / max|o|), so element * scale is within scale * 2^-12 of o * inv,
+// and (lse, scale) goes to lp[0..1]. DT + 1 store instructions, as the fp32 form, all
+// with the non-temporal hint (no later job of the launch reads them).
+template <int DT>
+__device__ __forceinline__ void store_row_h16(const f32x4 (&o)[DT], float inv, float lse, _Float16* hp, float* lp,
+                                              int G) {
+  float mx = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(o[dt][e]));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float k = mx > 0.f ? 1.f / mx : 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const f16x4 h = {(_Float16)(o[dt][0] * k), (_Float16)(o[dt][1] * k), (_Float16)(o[dt][2] * k),
+                     (_Float16)(o[dt][3] * k)};
+    __builtin_nontemporal_store(h, reinterpret_cast<f16x4*>(hp + 16 * dt + 4 * G));
+  }
+  const f32x2 ls = {lse, mx * inv};
+  __builtin_nontemporal_store(ls, reinterpret_cast<f32x2*>(lp));
+}
 
 __device__ __forceinline__ unsigned lds_addr(const unsigned char* p) {
   typedef __attribute__((address_space(3))) const unsigned char* lds_cptr;

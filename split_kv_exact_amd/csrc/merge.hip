@@ -41,7 +41,10 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <int D>
+// H16: partials stored as fp16 elements times a per-row scale, with (LSE, scale) pairs;
+// a lane then owns D/64 consecutive dimensions (one load per block row), and block b's
+// elements enter the sum weighted by w_b * scale_b while the denominator takes w_b.
+template <int D, bool H16>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int DPL = D / 64;
   const int64_t gw = int64_t(blockIdx.x) * WAVES + (threadIdx.x >> 6);
@@ -64,6 +67,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int nb = sq.nb;
   const int64_t r0 = sq.row_base + int64_t(kv) * nb * sq.rows + r;  // block b: r0 + b * rows
   const int64_t rs = sq.rows;
+  const _Float16* wh = reinterpret_cast<const _Float16*>(a.ws_o);
+  typedef _Float16 f16v __attribute__((ext_vector_type(DPL)));
+  typedef float f32v __attribute__((ext_vector_type(2)));
 
   // M = max_b LSE_b, then W = sum_b e^(LSE_b - M), lanes over blocks. The first blocks'
   // rows are requested before the maximum is formed (they do not depend on it).
@@ -72,18 +78,39 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int jb = min(j0 + u, cnt - 1);
-      const float* ob = a.ws_o + (r0 + (b0 + jb) * rs) * D;
+      const int64_t row = r0 + (b0 + jb) * rs;
+      if constexpr (H16) {
+        const f16v h = __builtin_nontemporal_load(reinterpret_cast<const f16v*>(wh + row * D + DPL * lane));
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) v[u][k] = __builtin_nontemporal_load(ob + lane + 64 * k);
+        for (int k = 0; k < DPL; ++k) v[u][k] = float(h[k]);
+      } else {
+        const float* ob = a.ws_o + row * D;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) v[u][k] = __builtin_nontemporal_load(ob + lane + 64 * k);
+      }
+    }
+  };
+  // Lane b's LSE_b (and row scale) of block b0 + lane.
+  auto stats = [&](int b, float& lse_b, float& scale_b) {
+    if constexpr (H16) {
+      const f32v p = b < nb ? __builtin_nontemporal_load(reinterpret_cast<const f32v*>(a.ws_lse + 2 * (r0 + b * rs)))
+                            : f32v{NEG_INF, 0.f};
+      lse_b = p[0];
+      scale_b = p[1];
+    } else {
+      lse_b = b < nb ? __builtin_nontemporal_load(a.ws_lse + r0 + b * rs) : NEG_INF;
+      scale_b = 1.f;
     }
   };
   load(0, 0, min(64, nb));
-  // Lane b keeps LSE_b of the first 64 blocks for the weights below.
-  const float lse0 = lane < nb ? __builtin_nontemporal_load(a.ws_lse + r0 + lane * rs) : NEG_INF;
+  // Lane b keeps LSE_b (and scale_b) of the first 64 blocks for the weights below.
+  float lse0, sc0;
+  stats(lane, lse0, sc0);
   float M = lse0;
   for (int b0 = 64; b0 < nb; b0 += 64) {
-    const int b = b0 + lane;
-    M = fmaxf(M, b < nb ? __builtin_nontemporal_load(a.ws_lse + r0 + b * rs) : NEG_INF);
+    float lb, sb;
+    stats(b0 + lane, lb, sb);
+    M = fmaxf(M, lb);
   }
   M = wave_max(M);
   float o[DPL];
@@ -93,16 +120,18 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   if (M != NEG_INF) {
     for (int b0 = 0; b0 < nb; b0 += 64) {
       const int b = b0 + lane;
-      const float lb = b0 == 0 ? lse0 : (b < nb ? a.ws_lse[r0 + b * rs] : NEG_INF);
+      float lb = lse0, sb = sc0;
+      if (b0 > 0) stats(b, lb, sb);
       const float wl = b < nb ? __builtin_amdgcn_exp2f((lb - M) * LOG2E) : 0.f;
       W += wl;
+      const float wo = H16 ? wl * sb : wl;  // weight of the block's stored elements
       const int cnt = min(64, nb - b0);
       for (int j0 = 0; j0 < cnt; j0 += UNROLL) {
         if (b0 > 0 || j0 > 0) load(b0, j0, cnt);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
           if (j0 + u < cnt) {
-            const float wb = __shfl(wl, j0 + u);
+            const float wb = __shfl(wo, j0 + u);
 #pragma unroll
             for (int k = 0; k < DPL; ++k) o[k] = __builtin_fmaf(wb, v[u][k], o[k]);
           }
@@ -113,8 +142,13 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
   const int64_t idx = (sq.q_base + i) * a.Hq + kv * a.g + hl;
+  if constexpr (H16) {
 #pragma unroll
-  for (int k = 0; k < DPL; ++k) a.out[idx * D + lane + 64 * k] = o[k] * inv;
+    for (int k = 0; k < DPL; ++k) a.out[idx * D + DPL * lane + k] = o[k] * inv;
+  } else {
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) a.out[idx * D + lane + 64 * k] = o[k] * inv;
+  }
   if (lane == 0) a.lse[idx] = W > 0.f ? M + __builtin_amdgcn_logf(W) * LN2 : NEG_INF;
 }
 
@@ -125,10 +159,14 @@ hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {
   const int64_t blocks = (a.total_rows + WAVES - 1) / WAVES;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks)), block(WAVES * 64);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, grid, block, 0, stream, a);
+  if (head_dim == 128 && a.h16)
+    hipLaunchKernelGGL((merge_kernel<128, true>), grid, block, 0, stream, a);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((merge_kernel<128, false>), grid, block, 0, stream, a);
+  else if (head_dim == 64 && a.h16)
+    hipLaunchKernelGGL((merge_kernel<64, true>), grid, block, 0, stream, a);
   else if (head_dim == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((merge_kernel<64, false>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

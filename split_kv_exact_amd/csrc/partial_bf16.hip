@@ -485,7 +485,7 @@ __device__ __forceinline__ void stage_compute(State<D>& st, int nt, bool two_ste
 // Normalise and store one row tile of a finished job (row li of the tile, dims
 // 16dt+4G..+3): Cfg<D>::STORES store instructions with every lane active. Lanes of
 // rows past the last query row store that row's values again.
-template <int D>
+template <int D, bool H16>
 __device__ __forceinline__ void write_tile(const State<D>& st, int t, const PartialArgs& a, const JobRec& j, int tile) {
   using C = Cfg<D>;
   const int lane = threadIdx.x & 63;
@@ -504,6 +504,10 @@ __device__ __forceinline__ void write_tile(const State<D>& st, int t, const Part
     lp = a.lse + idx;
   } else {
     const int64_t prow = j.ws_row + row;
+    if constexpr (H16) {
+      store_row_h16<C::DT>(st.o[t], inv, lse, reinterpret_cast<_Float16*>(a.ws_o) + prow * D, a.ws_lse + 2 * prow, G);
+      return;
+    }
     op = a.ws_o + prow * D;
     lp = a.ws_lse + prow;
   }
@@ -519,7 +523,7 @@ __device__ __forceinline__ void write_tile(const State<D>& st, int t, const Part
 // the LDS slot that stage used, then store every row tile. The slot is next written by
 // DMA only after the following iteration's barrier. Returns the number of store
 // instructions this wave issued.
-template <int D>
+template <int D, bool H16>
 __device__ __forceinline__ int finish_job(State<D>& st, const PartialArgs& a, const Work& w, const JobRec& j,
                                           unsigned char* slot, float c) {
   using C = Cfg<D>;
@@ -528,7 +532,7 @@ __device__ __forceinline__ int finish_job(State<D>& st, const PartialArgs& a, co
   if (w.Wk == 1) {
 #pragma unroll
     for (int t = 0; t < RTW; ++t)
-      if (t < w.nt) write_tile<D>(st, t, a, j, j.tile_lo + w.rg + t * Wr);
+      if (t < w.nt) write_tile<D, H16>(st, t, a, j, j.tile_lo + w.rg + t * Wr);
     return w.nt * C::STORES;
   }
   // Two key slices per row group; one round per tile index (<= Wr records each). The
@@ -568,7 +572,7 @@ __device__ __forceinline__ int finish_job(State<D>& st, const PartialArgs& a, co
             st.o[t][dt][q4] = st.o[t][dt][q4] * a1 + rec[(3 + dt * 4 + q4) * 64 + lane] * a2;
         st.m[t] = ms;
       }
-      write_tile<D>(st, t, a, j, j.tile_lo + w.rg + t * Wr);
+      write_tile<D, H16>(st, t, a, j, j.tile_lo + w.rg + t * Wr);
     }
   }
   return w.ks == 0 ? w.nt * C::STORES : 0;
@@ -608,7 +612,7 @@ __device__ __forceinline__ void started_pop(Started& S) {
 
 // QUEUE: after its static list, the workgroup draws chunks of the shared tail. A
 // template parameter, so that the static kernel holds no queue code at all.
-template <int D, bool QUEUE>
+template <int D, bool QUEUE, bool H16>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void partial_bf16_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const int32_t* __restrict__ wjobs,
                          const int32_t* __restrict__ job_ptr, const int32_t* __restrict__ chunk_ptr) {
@@ -772,7 +776,7 @@ void partial_bf16_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const i
       stage_compute<D>(st, w.nt, w.tkw == TK, ka, va, key0, need_mask, c, inv_c);
     }
     if (jj + 1 == w.nst) {
-      const int s = finish_job<D>(st, a, w, jobs[w.job], slot, c);
+      const int s = finish_job<D, H16>(st, a, w, jobs[w.job], slot, c);
       c1 += s;
       c2 += s;
       reset<D>(st);
@@ -809,21 +813,27 @@ void partial_bf16_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const i
 
 }  // namespace
 
-hipError_t launch_partial_bf16(const PartialArgs& a, int head_dim, hipStream_t stream) {
+template <int D, bool H16>
+static void launch_variant(const PartialArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_workers), block(NW * 64);
-  if (head_dim == 128) {
-    if (a.queue)
-      hipLaunchKernelGGL((partial_bf16_kernel<128, true>), grid, block, 0, stream, a, a.jobs, a.wjobs, a.job_ptr, a.chunk_ptr);
-    else
-      hipLaunchKernelGGL((partial_bf16_kernel<128, false>), grid, block, 0, stream, a, a.jobs, a.wjobs, a.job_ptr, a.chunk_ptr);
-  } else if (head_dim == 64) {
-    if (a.queue)
-      hipLaunchKernelGGL((partial_bf16_kernel<64, true>), grid, block, 0, stream, a, a.jobs, a.wjobs, a.job_ptr, a.chunk_ptr);
-    else
-      hipLaunchKernelGGL((partial_bf16_kernel<64, false>), grid, block, 0, stream, a, a.jobs, a.wjobs, a.job_ptr, a.chunk_ptr);
-  } else {
+  if (a.queue)
+    hipLaunchKernelGGL((partial_bf16_kernel<D, true, H16>), grid, block, 0, stream, a, a.jobs, a.wjobs, a.job_ptr,
+                       a.chunk_ptr);
+  else
+    hipLaunchKernelGGL((partial_bf16_kernel<D, false, H16>), grid, block, 0, stream, a, a.jobs, a.wjobs, a.job_ptr,
+                       a.chunk_ptr);
+}
+
+hipError_t launch_partial_bf16(const PartialArgs& a, int head_dim, hipStream_t stream) {
+  // The partial format is a template parameter, so that the store path it selects adds
+  // nothing to the streaming loop's scalar registers (the loop runs near the SGPR limit;
+  // more live scalars spill to VGPR lanes inside it).
+  if (head_dim == 128)
+    a.h16 ? launch_variant<128, true>(a, stream) : launch_variant<128, false>(a, stream);
+  else if (head_dim == 64)
+    a.h16 ? launch_variant<64, true>(a, stream) : launch_variant<64, false>(a, stream);
+  else
     return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
 

@@ -372,7 +372,7 @@ __device__ __forceinline__ int tile_row(const JobRec& j, int tile, int li) {
 
 // Normalise and store row tile t (tile index `tile` of the job): DT + 1 store
 // instructions with every lane active.
-template <int D>
+template <int D, bool H16>
 __device__ __forceinline__ void write_tile(const State<D>& st, int t, const PartialArgs& a, const JobRec& j, int tile) {
   using C = Cfg<D>;
   const int lane = threadIdx.x & 63;
@@ -391,6 +391,10 @@ __device__ __forceinline__ void write_tile(const State<D>& st, int t, const Part
     lp = a.lse + idx;
   } else {
     const int64_t prow = j.ws_row + row;
+    if constexpr (H16) {
+      store_row_h16<C::DT>(st.o[t], inv, lse, reinterpret_cast<_Float16*>(a.ws_o) + prow * D, a.ws_lse + 2 * prow, G);
+      return;
+    }
     op = a.ws_o + prow * D;
     lp = a.ws_lse + prow;
   }
@@ -402,7 +406,7 @@ __device__ __forceinline__ void write_tile(const State<D>& st, int t, const Part
 
 // PARTIAL: the launch has passes of fewer than 16 row tiles, whose waves skip a second
 // tile past the pass; without it every wave always computes two tiles (no branches).
-template <int D, bool PARTIAL>
+template <int D, bool PARTIAL, bool H16>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void partial_mma_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const int32_t* __restrict__ wjobs,
                         const int32_t* __restrict__ job_ptr, const int32_t* __restrict__ split_ptr) {
@@ -549,8 +553,8 @@ void partial_mma_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const in
     if (issue()) cnt[AHEAD - 1] = 0;
     if (++jj == nst) {
       const JobRec j = jobs[wjobs[ci]];
-      write_tile<D>(st, 0, a, j, j.tile_lo + wave);
-      if (two) write_tile<D>(st, 1, a, j, j.tile_lo + wave + 8);
+      write_tile<D, H16>(st, 0, a, j, j.tile_lo + wave);
+      if (two) write_tile<D, H16>(st, 1, a, j, j.tile_lo + wave + 8);
 #pragma unroll
       for (int x = 0; x <= AHEAD; ++x) cnt[x] += (two ? 2 : 1) * C::STORES;
       reset<D>(st);
@@ -568,24 +572,25 @@ void partial_mma_kernel(PartialArgs a, const JobRec* __restrict__ jobs, const in
 
 }  // namespace
 
-hipError_t launch_partial_mma(const PartialArgs& a, int head_dim, bool partial_passes, hipStream_t stream) {
+template <int D, bool H16>
+static void launch_variant(const PartialArgs& a, bool partial_passes, hipStream_t stream) {
   const dim3 grid(a.num_workers), block(NW * 64);
-#define SKV_LAUNCH(DD, P) \
-  hipLaunchKernelGGL((partial_mma_kernel<DD, P>), grid, block, 0, stream, a, a.jobs, a.wjobs, a.job_ptr, a.split_ptr)
-  if (head_dim == 128) {
-    if (partial_passes)
-      SKV_LAUNCH(128, true);
-    else
-      SKV_LAUNCH(128, false);
-  } else if (head_dim == 64) {
-    if (partial_passes)
-      SKV_LAUNCH(64, true);
-    else
-      SKV_LAUNCH(64, false);
-  } else {
+  if (partial_passes)
+    hipLaunchKernelGGL((partial_mma_kernel<D, true, H16>), grid, block, 0, stream, a, a.jobs, a.wjobs, a.job_ptr,
+                       a.split_ptr);
+  else
+    hipLaunchKernelGGL((partial_mma_kernel<D, false, H16>), grid, block, 0, stream, a, a.jobs, a.wjobs, a.job_ptr,
+                       a.split_ptr);
+}
+
+hipError_t launch_partial_mma(const PartialArgs& a, int head_dim, bool partial_passes, hipStream_t stream) {
+  // The partial format is a template parameter, as in the streaming kernel.
+  if (head_dim == 128)
+    a.h16 ? launch_variant<128, true>(a, partial_passes, stream) : launch_variant<128, false>(a, partial_passes, stream);
+  else if (head_dim == 64)
+    a.h16 ? launch_variant<64, true>(a, partial_passes, stream) : launch_variant<64, false>(a, partial_passes, stream);
+  else
     return hipErrorInvalidValue;
-  }
-#undef SKV_LAUNCH
   return hipGetLastError();
 }
 

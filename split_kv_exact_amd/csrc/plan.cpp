@@ -41,6 +41,8 @@ bool validate_problem(const splitkv_problem* p, std::string* why) {
   if (p->granularity != SPLITKV_UNIT_SEQ_BLOCK_KVHEAD && p->granularity != SPLITKV_UNIT_SEQ_BLOCK)
     return fail("unknown granularity");
   if (p->cost_ridge_rows < 0 || p->cost_ridge_rows > (1 << 30)) return fail("cost_ridge_rows must be in [0, 2^30]");
+  if (p->partial_format != SPLITKV_PARTIAL_F32 && p->partial_format != SPLITKV_PARTIAL_F16_ROWSCALE)
+    return fail("unknown partial_format");
   if (p->xcd_speed)
     for (int x = 0; x < 8; ++x)
       if (p->xcd_speed[x] < 1) return fail("xcd_speed entries must be >= 1");
@@ -90,6 +92,7 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   pl->causal = p->causal;
   pl->granularity = p->granularity;
   pl->ridge = p->cost_ridge_rows;
+  pl->pfmt = p->partial_format;
   pl->xcd_speed.clear();
   if (p->xcd_speed) pl->xcd_speed.assign(p->xcd_speed, p->xcd_speed + 8);
   pl->g = p->num_q_heads / p->num_kv_heads;
@@ -133,8 +136,11 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   pl->ws_lse_offset = align16(uint64_t(row_base) * pl->D * sizeof(float));
   // The LSE area also holds the backward pass's two per-row values (D and the LSE in
   // base 2), 2 * sum_s q_s * Hq floats, more than the partial rows of one-block sequences.
+  // The output area keeps its fp32 size with fp16 partials too: the backward pass puts
+  // fp32 dQ parts there. With fp16 partials the LSE area holds (LSE, scale) pairs.
+  const uint64_t lse_words = uint64_t(row_base) * (pl->pfmt == SPLITKV_PARTIAL_F16_ROWSCALE ? 2 : 1);
   pl->ws_bytes = pl->ws_lse_offset +
-                 align16(std::max<uint64_t>(uint64_t(row_base), 2 * uint64_t(q_base) * uint64_t(pl->Hq)) * sizeof(float));
+                 align16(std::max<uint64_t>(lse_words, 2 * uint64_t(q_base) * uint64_t(pl->Hq)) * sizeof(float));
 
   // Units in enumeration order, with their costs.
   pl->u_seq.clear();

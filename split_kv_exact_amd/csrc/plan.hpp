@@ -13,6 +13,7 @@ struct splitkv_plan_s {
   // Problem.
   int32_t S = 0, Hq = 0, Hkv = 0, D = 0, B = 0, m = 0, causal = 0, granularity = 0, g = 0;
   int32_t ridge = 0;  // cost_ridge_rows of the problem
+  int32_t pfmt = 0;   // partial_format of the problem (splitkv_partial_format)
   std::vector<int32_t> xcd_speed;    // [8] relative speeds, or empty
   std::vector<int32_t> slot_worker;  // the plan worker run by workgroup s
   std::vector<int64_t> kv_lens;

@@ -4,11 +4,13 @@ effective_bytes: what the whole split-KV attention must move at least once:
     Q + K + V (each stored element counted once) + O (fp32) + LSE (fp32).
 partial_kernel_bytes: what one launch of the partial-attention kernel must move:
     per unit (sequence s, block b, KV heads), the block's K and V, the unit's query
-    rows of Q, and its fp32 partial output and LSE.
+    rows of Q, and its partial output and LSE in the plan's partial format.
 merge_kernel_bytes: partials read once, O and LSE written once.
-partial_traffic_bytes: the fp32 partial outputs and LSEs written by the partial
-    kernel and read back by the merge, 2 * partial_rows * (D + 1) * 4. This is traffic
-    the exact merge costs, never credited as useful bytes.
+partial_traffic_bytes: the partial outputs and LSEs written by the partial kernel and
+    read back by the merge, 2 * partial_rows * row bytes: (D + 1) * 4 for fp32 partials
+    (fp32 inputs), D * 2 + 8 for row-scaled fp16 partials (bf16 inputs: fp16 elements,
+    the LSE and the row scale). This is traffic the exact merge costs, never credited
+    as useful bytes.
 flops: 2 flops per multiply-add of QK^T and of PV over the (query, key) pairs the
     mask keeps: 4 * D * Hq * sum_s visible_pairs_s.
 """
@@ -54,15 +56,20 @@ def partial_rows(wl) -> int:
 
 def partial_kernel_bytes(wl) -> int:
     q_per_unit = sum(wl.num_blocks(s) * wl.q_lens[s] * wl.num_q_heads for s in range(wl.batch))
-    return kv_bytes(wl) + q_per_unit * wl.head_dim * wl.elem_bytes + partial_rows(wl) * (wl.head_dim + 1) * 4
+    return kv_bytes(wl) + q_per_unit * wl.head_dim * wl.elem_bytes + partial_rows(wl) * partial_row_bytes(wl)
+
+
+def partial_row_bytes(wl) -> int:
+    """Bytes of one stored partial row in the format the plans of this workload use."""
+    return wl.head_dim * 2 + 8 if wl.dtype == "bfloat16" else (wl.head_dim + 1) * 4
 
 
 def partial_traffic_bytes(wl) -> int:
-    return 2 * partial_rows(wl) * (wl.head_dim + 1) * 4
+    return 2 * partial_rows(wl) * partial_row_bytes(wl)
 
 
 def merge_kernel_bytes(wl) -> int:
-    return partial_rows(wl) * (wl.head_dim + 1) * 4 + out_bytes(wl)
+    return partial_rows(wl) * partial_row_bytes(wl) + out_bytes(wl)
 
 
 def roofline_seconds(wl) -> float:

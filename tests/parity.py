@@ -76,6 +76,32 @@ def partial_row(wl, s, b, kappa, r):
     return base + (kappa * wl.num_blocks(s) + b) * rows + r
 
 
+def assert_fused_matches_merge(wl, plan, out_f, lse_f, out_m, lse_m) -> None:
+    """The fused call against partial_attn + merge on the same plan (torch tensors).
+
+    The fused call writes the rows of single-block sequences from its fp32 accumulators;
+    the separate merge reads them back from the stored partials. Every LSE and every
+    multi-block row is the same bits in both; single-block rows too with fp32 partials.
+    With row-scaled fp16 partials a single-block row differs by the element's fp16
+    rounding: at most half an fp16 step at 1.0 (2^-12) of the row's largest |O|, plus
+    fp32 rounding of the scale (the 1.002 factor)."""
+    import torch
+
+    assert torch.equal(lse_f, lse_m), "LSE differs between the fused call and the merge"
+    if plan.info()["partial_format"] == 0:
+        assert torch.equal(out_f, out_m), "fp32 partials: the fused call and the merge differ"
+        return
+    single = torch.zeros(wl.total_q, dtype=torch.bool)
+    for s, o in enumerate(offsets(wl.q_lens)[:-1]):
+        if wl.num_blocks(s) == 1:
+            single[o:o + wl.q_lens[s]] = True
+    single = single.to(out_f.device)
+    assert torch.equal(out_f[~single], out_m[~single]), "multi-block rows differ"
+    a, b = out_f[single], out_m[single]
+    bound = a.abs().amax(dim=-1, keepdim=True) * (2.0 ** -12 * 1.002)
+    assert bool(((a - b).abs() <= bound).all()), "single-block rows beyond the fp16 partial bound"
+
+
 def scale_of(wl):
     return 1.0 / math.sqrt(wl.head_dim)
 

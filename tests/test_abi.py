@@ -224,6 +224,34 @@ def test_workspace_holds_the_backward_row_values():
     assert many["workspace_bytes"] == many["ws_lse_offset"] + 4 * many["partial_rows"]
 
 
+def test_partial_formats():
+    """Row-scaled fp16 partials keep an (LSE, scale) pair per row: the LSE area doubles,
+    the element area keeps its fp32 size (the backward pass stores fp32 parts there)."""
+    f32 = splitkv_plan([640, 320], [7, 3], 8, 2, 128, 64, 8).info()
+    h16 = splitkv_plan([640, 320], [7, 3], 8, 2, 128, 64, 8,
+                       partial_format=L.SPLITKV_PARTIAL_F16_ROWSCALE).info()
+    assert f32["partial_format"] == L.SPLITKV_PARTIAL_F32
+    assert h16["partial_format"] == L.SPLITKV_PARTIAL_F16_ROWSCALE
+    assert h16["partial_rows"] == f32["partial_rows"] and h16["ws_lse_offset"] == f32["ws_lse_offset"]
+    assert h16["workspace_bytes"] == h16["ws_lse_offset"] + 8 * h16["partial_rows"]
+    with pytest.raises(SplitKVError) as e:
+        splitkv_plan([10], [2], 4, 2, 128, 64, 8, partial_format=2)
+    assert e.value.status == L.SPLITKV_ERR_INVALID_ARG and "partial_format" in str(e.value)
+
+
+def test_fp32_inputs_need_fp32_partials(lib):
+    p, keep = _problem([100, 40], [3, 1])
+    p.partial_format = L.SPLITKV_PARTIAL_F16_ROWSCALE
+    h = ctypes.c_void_p()
+    assert lib.splitkv_plan(ctypes.byref(p), ctypes.byref(h)) == 0
+    inf = L.PlanInfo()
+    assert lib.splitkv_plan_info_get(h, ctypes.byref(inf)) == 0
+    ws, dp = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE)
+    st = lib.splitkv_partial_attn(h, dp, ctypes.byref(_inputs(dtype=L.SPLITKV_F32)), ws, inf.workspace_bytes, None)
+    assert st == L.SPLITKV_ERR_UNSUPPORTED and b"partial_format" in lib.splitkv_last_error()
+    lib.splitkv_plan_destroy(h)
+
+
 @pytest.mark.parametrize("q, g, jobs, partial", [
     ([3, 1], 2, False, 0),          # every job below 8 row tiles: no matrix-path launch
     ([64, 125, 20], 4, True, 0),    # 256 and 500 rows: passes of 16 tiles only

@@ -67,6 +67,11 @@ def test_byte_and_flop_accounting_by_hand():
     # Partial rows: sequence 0 has 2 blocks x 2 KV heads x (2 queries x g 2), sequence 1
     # one block x 2 x (3 x 2).
     assert M.partial_rows(wl) == 2 * 2 * 4 + 1 * 2 * 6
-    # Every unit reads its block's query rows: blocks x q x Hq elements.
-    assert M.partial_kernel_bytes(wl) == kv + (2 * 2 * 4 + 1 * 3 * 4) * 8 * 2 + 28 * 9 * 4
-    assert M.merge_kernel_bytes(wl) == 28 * 9 * 4 + out
+    # Every unit reads its block's query rows: blocks x q x Hq elements. bf16 inputs keep
+    # their partials as fp16 elements with an fp32 (LSE, scale) pair: 8 * 2 + 8 bytes a row.
+    assert M.partial_kernel_bytes(wl) == kv + (2 * 2 * 4 + 1 * 3 * 4) * 8 * 2 + 28 * (8 * 2 + 8)
+    assert M.merge_kernel_bytes(wl) == 28 * (8 * 2 + 8) + out
+    assert M.partial_traffic_bytes(wl) == 2 * 28 * (8 * 2 + 8)
+    f32 = Workload(name="t", dtype="float32", kv_lens=(6, 3), q_lens=(2, 3), num_q_heads=4, num_kv_heads=2,
+                   head_dim=8, block_len=4, num_workers=3)
+    assert M.partial_traffic_bytes(f32) == 2 * 28 * 9 * 4

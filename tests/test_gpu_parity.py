@@ -15,7 +15,7 @@ import torch
 
 import split_kv_exact_amd as skv
 from oracle import attend_rows, attention_ref, partials_ref
-from tests.parity import Diff, assert_within, compare, compare_whole, offsets, partial_row, say, scale_of
+from tests.parity import Diff, assert_fused_matches_merge, assert_within, compare, compare_whole, offsets, partial_row, say, scale_of
 from workloads import Workload, get_workload, make_qkv, widen_to_f64
 
 pytestmark = pytest.mark.gpu
@@ -113,8 +113,8 @@ def test_small_cases_against_full_oracle(wl):
     assert_within(d_merge, wl.dtype, "partial+merge")
     assert_within(d_fused, wl.dtype, "fused")
     # The fused call writes single-block sequences directly; all other rows go through
-    # the same merge, so both paths give identical bits.
-    assert torch.equal(out_m, out_f) and torch.equal(lse_m, lse_f)
+    # the same merge.
+    assert_fused_matches_merge(wl, plan, out_f, lse_f, out_m, lse_m)
     # Every partial against the oracle's per-block partials.
     parts = partials_ref(qh, kh, vh, wl.kv_lens, wl.q_lens, wl.num_q_heads, wl.num_kv_heads, wl.block_len,
                          wl.causal)
@@ -143,9 +143,44 @@ def test_bitwise_identical_across_worker_counts():
     for m in (1, 3, 16, 256):
         _, _, out_m, lse_m, out_f, lse_f = _run_all(wl, q, k, v, m)
         if ref is None:
-            ref = (out_f.clone(), lse_f.clone())
+            ref = (out_f.clone(), lse_f.clone(), out_m.clone(), lse_m.clone())
         assert torch.equal(out_f, ref[0]) and torch.equal(lse_f, ref[1]), f"m={m}"
-        assert torch.equal(out_m, ref[0])
+        assert torch.equal(out_m, ref[2]) and torch.equal(lse_m, ref[3]), f"m={m}"
+
+
+@pytest.mark.parametrize("name", ["ragged_bf16_d128", "ragged_bf16_d64", "many_rows", "edge_q_equals_n",
+                                  "many_short_sequences"])
+def test_bf16_partial_formats_agree(name):
+    """bf16 inputs under both partial formats: fp32 partials meet the oracle, the LSEs of
+    the two formats are the same bits, and each fp16 element, decoded with its row scale,
+    lies within half an fp16 step at 1.0 (2^-12) of the row's largest |O| from the fp32
+    partial."""
+    wl = next(w for w in SMALL if w.name == name)
+    say(f"[gpu] partial formats on {wl.name}")
+    q, k, v = make_qkv(wl, "cuda")
+    got = {}
+    for fmt in (skv.SPLITKV_PARTIAL_F32, skv.SPLITKV_PARTIAL_F16_ROWSCALE):
+        plan = skv.plan_for(wl, partial_format=fmt)
+        assert plan.info()["partial_format"] == fmt
+        dev_plan = skv.splitkv_plan_upload(plan)
+        ws = skv.workspace(plan)
+        ws.fill_(float("nan"))
+        skv.splitkv_partial_attn(plan, dev_plan, q, k, v, ws)
+        out, lse = skv.splitkv_attn(plan, dev_plan, q, k, v)
+        torch.cuda.synchronize()
+        wo, wlse = skv.workspace_views(plan, ws)
+        got[fmt] = (wo.cpu().numpy(), wlse.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy())
+    f32, h16 = got[skv.SPLITKV_PARTIAL_F32], got[skv.SPLITKV_PARTIAL_F16_ROWSCALE]
+    O, L = attention_ref(widen_to_f64(q), widen_to_f64(k), widen_to_f64(v), wl.kv_lens, wl.q_lens,
+                         wl.num_q_heads, wl.num_kv_heads, wl.causal)
+    d = compare(f32[2], O, f32[3], L)
+    say(f"  fp32 partials, fused: {d}")
+    assert_within(d, wl.dtype, "fused with fp32 partials")
+    assert not np.any(np.isnan(f32[1])) and np.array_equal(f32[1], h16[1])
+    rowmax = np.abs(f32[0]).max(axis=1, keepdims=True)
+    err = np.abs(h16[0] - f32[0])
+    assert np.all(err <= rowmax * (2.0 ** -12 * 1.001) + 1e-30), float((err / np.maximum(rowmax, 1e-30)).max())
+    assert np.array_equal(f32[3], h16[3])  # the merged LSE depends on the partial LSEs only
 
 
 def test_repeated_calls_reuse_buffers():
@@ -265,7 +300,7 @@ def _full(key):
     skv.splitkv_partial_attn(plan, dev_plan, q, k, v, ws)
     out2, lse2 = skv.splitkv_merge(plan, dev_plan, ws)
     torch.cuda.synchronize()
-    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    assert_fused_matches_merge(wl, plan, out, lse, out2, lse2)
     del out2, lse2
     _FULL[key] = (wl, q, k, v, plan, ws, out, lse)
     return _FULL[key]
