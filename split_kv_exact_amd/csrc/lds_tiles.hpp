@@ -30,9 +30,12 @@ __device__ __forceinline__ int swz_tr(int row, int c) { return c ^ ((2 * row) & 
 // bf16 kernels; the row's other elements are on the lanes 16 and 32 apart), before
 // normalisation by inv. The row's scale is its largest |o * inv|; each element is
 // stored as fp16(o / max|o|), so element * scale is within scale * 2^-12 of o * inv,
-// and (lse, scale) goes to lp[0..1]. DT + 1 store instructions, as the fp32 form, all
-// with the non-temporal hint (no later job of the launch reads them).
-template <int DT>
+// and (lse, scale) goes to lp[0..1]. DT + 1 store instructions, as the fp32 form.
+// NT: the elements carry the non-temporal hint (the pair always does). Each element
+// store writes 32-byte pieces of 16 rows; the matrix-core kernel stores them cached,
+// because there non-temporal pieces reached HBM as separate partial-line writes
+// (measured: 2.2 times the elements' bytes), while cached ones merge in L2.
+template <int DT, bool NT>
 __device__ __forceinline__ void store_row_h16(const f32x4 (&o)[DT], float inv, float lse, _Float16* hp, float* lp,
                                               int G) {
   float mx = 0.f;
@@ -47,7 +50,10 @@ __device__ __forceinline__ void store_row_h16(const f32x4 (&o)[DT], float inv, f
   for (int dt = 0; dt < DT; ++dt) {
     const f16x4 h = {(_Float16)(o[dt][0] * k), (_Float16)(o[dt][1] * k), (_Float16)(o[dt][2] * k),
                      (_Float16)(o[dt][3] * k)};
-    __builtin_nontemporal_store(h, reinterpret_cast<f16x4*>(hp + 16 * dt + 4 * G));
+    if constexpr (NT)
+      __builtin_nontemporal_store(h, reinterpret_cast<f16x4*>(hp + 16 * dt + 4 * G));
+    else
+      *reinterpret_cast<f16x4*>(hp + 16 * dt + 4 * G) = h;
   }
   const f32x2 ls = {lse, mx * inv};
   __builtin_nontemporal_store(ls, reinterpret_cast<f32x2*>(lp));

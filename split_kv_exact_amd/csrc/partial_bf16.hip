@@ -505,7 +505,7 @@ __device__ __forceinline__ void write_tile(const State<D>& st, int t, const Part
   } else {
     const int64_t prow = j.ws_row + row;
     if constexpr (H16) {
-      store_row_h16<C::DT>(st.o[t], inv, lse, reinterpret_cast<_Float16*>(a.ws_o) + prow * D, a.ws_lse + 2 * prow, G);
+      store_row_h16<C::DT, true>(st.o[t], inv, lse, reinterpret_cast<_Float16*>(a.ws_o) + prow * D, a.ws_lse + 2 * prow, G);
       return;
     }
     op = a.ws_o + prow * D;
