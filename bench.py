@@ -693,33 +693,40 @@ def _bench_backward(skv, M, wl, q, k, v, stream, args):
     do = torch.randn(q.shape, generator=gen, device=q.device, dtype=torch.float32).to(q.dtype)
     out, lse = skv.splitkv_attn(plan, dev_plan, q, k, v, ws)
     dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
-    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    res = {}
+    # dK and dV as fp32, then as bf16 (the input dtype); dQ is fp32 in both.
+    for dt, key in ((torch.float32, "fp32_dkv"), (torch.bfloat16, "bf16_dkv")):
+        dk = torch.empty(k.shape, dtype=dt, device=q.device)
+        dv = torch.empty(v.shape, dtype=dt, device=q.device)
 
-    def bstep():
-        skv.splitkv_attn_backward(plan, dev_plan, q, k, v, do, out, lse, ws, dq, dk, dv)
+        def bstep():
+            skv.splitkv_attn_backward(plan, dev_plan, q, k, v, do, out, lse, ws, dq, dk, dv)
 
-    # Untimed calls while the clocks settle (as for the forward), then the warmups.
-    t_settle = time.perf_counter()
-    while time.perf_counter() - t_settle < args.settle_ms * 1e-3:
-        bstep()
-        torch.cuda.synchronize()
-    for _ in range(max(1, args.warmup)):
-        bstep()
-    ms = _time_loop(bstep, max(3, min(args.steps, 10)), stream)
-    fl, by = M.backward_flops(wl), M.backward_bytes(wl)
-    tr = M.backward_roofline_seconds(wl)
-    bound = "mfma" if fl / (M.PEAK_BF16_MFMA_TFLOPS * 1e12) >= by / (M.PEAK_HBM_GBS * 1e9) else "hbm"
-    return {
-        "ms_per_call": round(ms, 5),
-        "tflops": round(fl / (ms * 1e-3) / 1e12, 3),
-        "gbs": round(by / (ms * 1e-3) / 1e9, 2),
-        "flops": fl,
-        "bytes": by,
-        "bound": bound,
-        "roofline_fraction": round(tr / (ms * 1e-3), 4),
-        "note": "flops 10*D per visible (row, key) pair; bytes Q, K, V, dO, O, LSE read once, dQ, dK, dV written",
-    }
+        # Untimed calls while the clocks settle (as for the forward), then the warmups.
+        t_settle = time.perf_counter()
+        while time.perf_counter() - t_settle < args.settle_ms * 1e-3:
+            bstep()
+            torch.cuda.synchronize()
+        for _ in range(max(1, args.warmup)):
+            bstep()
+        ms = _time_loop(bstep, max(3, min(args.steps, 10)), stream)
+        dkv_bytes = dk.element_size()
+        fl, by = M.backward_flops(wl), M.backward_bytes(wl, dkv_bytes)
+        tr = M.backward_roofline_seconds(wl, dkv_bytes)
+        bound = "mfma" if fl / (M.PEAK_BF16_MFMA_TFLOPS * 1e12) >= by / (M.PEAK_HBM_GBS * 1e9) else "hbm"
+        res[key] = {
+            "ms_per_call": round(ms, 5),
+            "tflops": round(fl / (ms * 1e-3) / 1e12, 3),
+            "gbs": round(by / (ms * 1e-3) / 1e9, 2),
+            "flops": fl,
+            "bytes": by,
+            "bound": bound,
+            "roofline_fraction": round(tr / (ms * 1e-3), 4),
+        }
+        del dk, dv
+    res["note"] = ("flops 10*D per visible (row, key) pair; bytes Q, K, V, dO, O, LSE read once, dQ (fp32), "
+                   "dK, dV (fp32 or bf16) written")
+    return res
 
 
 if __name__ == "__main__":

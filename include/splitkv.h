@@ -56,7 +56,7 @@ extern "C" {
 #endif
 
 #define SPLITKV_VERSION_MAJOR 0
-#define SPLITKV_VERSION_MINOR 7
+#define SPLITKV_VERSION_MINOR 8
 
 typedef enum {
   SPLITKV_OK = 0,
@@ -284,9 +284,12 @@ typedef struct {
   int64_t do_stride_tok, do_stride_head; /* its strides in elements (multiples of 16 bytes)     */
   const float *out;                      /* the forward's O [sum q, Hq, D], contiguous          */
   const float *lse;                      /* the forward's LSE [sum q, Hq] (natural log)          */
-  float *dq;                             /* written: dQ [sum q, Hq, D], contiguous               */
-  float *dk;                             /* written: dK [sum n, Hkv, D], contiguous              */
-  float *dv;                             /* written: dV [sum n, Hkv, D], contiguous              */
+  float *dq;                             /* written: dQ [sum q, Hq, D] fp32, contiguous          */
+  void *dk;                              /* written: dK [sum n, Hkv, D], contiguous, dkv_dtype   */
+  void *dv;                              /* written: dV [sum n, Hkv, D], contiguous, dkv_dtype   */
+  int32_t dkv_dtype;                     /* splitkv_dtype of dK and dV: SPLITKV_F32 (0) or       *
+                                          * SPLITKV_BF16 (1, each value rounded to nearest even  *
+                                          * from the fp32 sum; half the bytes written)           */
 } splitkv_grads;
 
 /* Backward pass of split-KV attention: dQ, dK, dV of sum(dO * O) with respect to Q, K
@@ -299,10 +302,11 @@ typedef struct {
  *   D_i = <dO_i, O_i>, P = e^(scale q.k - LSE), dS = P (dO.v - D),
  *   dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO,
  * with dK and dV summed over the query heads of each KV head. bf16 inputs only;
- * gradients fp32. The workspace (splitkv_plan_info.workspace_bytes) holds the dQ parts,
+ * every sum is fp32; dQ is stored as fp32, dK and dV as grads->dkv_dtype. The workspace (splitkv_plan_info.workspace_bytes) holds the dQ parts,
  * D and the LSE in base 2. The fields schedule and worker_clock of in are not used.
- * Errors: INVALID_ARG (NULL or misaligned pointers, bad strides), UNSUPPORTED (fp32
- * inputs, head_dim other than 64 or 128, bf16 strides beyond 2^24), WORKSPACE, HIP. */
+ * Errors: INVALID_ARG (NULL or misaligned pointers, bad strides, dkv_dtype not a
+ * splitkv_dtype), UNSUPPORTED (fp32 inputs, head_dim other than 64 or 128, bf16 strides
+ * beyond 2^24), WORKSPACE, HIP. */
 int splitkv_attn_backward(const splitkv_plan_t *plan, const void *dev_plan, const splitkv_inputs *in,
                           const splitkv_grads *grads, float *ws, size_t ws_bytes, void *hip_stream);
 

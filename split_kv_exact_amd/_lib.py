@@ -122,6 +122,7 @@ class Grads(ctypes.Structure):
         ("dq", ctypes.c_void_p),
         ("dk", ctypes.c_void_p),
         ("dv", ctypes.c_void_p),
+        ("dkv_dtype", ctypes.c_int32),
     ]
 
 

@@ -297,9 +297,10 @@ def splitkv_attn_scratch(plan: Plan, dev_plan, q, k, v, out=None, lse=None, scal
 
 
 def splitkv_attn_backward(plan: Plan, dev_plan, q, k, v, do, out, lse, ws=None, dq=None, dk=None, dv=None,
-                          scale: float = 0.0, stream=None):
-    """Gradients dQ, dK, dV (fp32) of sum(do * out) at the forward's ``out`` and ``lse``
-    (``splitkv_attn_backward``; bf16 inputs)."""
+                          scale: float = 0.0, stream=None, dkv_dtype=None):
+    """Gradients dQ, dK, dV of sum(do * out) at the forward's ``out`` and ``lse``
+    (``splitkv_attn_backward``; bf16 inputs). dQ is float32; dK and dV are float32 or
+    bfloat16 (``dkv_dtype``, else the dtype of a given ``dk``, else float32)."""
     torch = _torch()
     _check_shapes(plan, q, k, v)
     if do.shape != q.shape or do.dtype != q.dtype or do.stride(2) != 1:
@@ -311,16 +312,21 @@ def splitkv_attn_backward(plan: Plan, dev_plan, q, k, v, do, out, lse, ws=None, 
         ws = workspace(plan, q.device)
     if dq is None:
         dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if dkv_dtype is None:
+        dkv_dtype = dk.dtype if dk is not None else torch.float32
+    if dkv_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("dkv_dtype must be torch.float32 or torch.bfloat16")
     if dk is None:
-        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+        dk = torch.empty(k.shape, dtype=dkv_dtype, device=q.device)
     if dv is None:
-        dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
-    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        if t.shape != ref.shape or t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous float32 tensor shaped like {name[1]}")
+        dv = torch.empty(v.shape, dtype=dkv_dtype, device=q.device)
+    for name, t, ref, dt in (("dq", dq, q, torch.float32), ("dk", dk, k, dkv_dtype), ("dv", dv, v, dkv_dtype)):
+        if t.shape != ref.shape or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor shaped like {name[1]}")
     inp = _inputs(q, k, v, scale)
     gr = L.Grads(d_out=do.data_ptr(), do_stride_tok=do.stride(0), do_stride_head=do.stride(1), out=out.data_ptr(),
-                 lse=lse.data_ptr(), dq=dq.data_ptr(), dk=dk.data_ptr(), dv=dv.data_ptr())
+                 lse=lse.data_ptr(), dq=dq.data_ptr(), dk=dk.data_ptr(), dv=dv.data_ptr(),
+                 dkv_dtype=L.SPLITKV_BF16 if dkv_dtype == torch.bfloat16 else L.SPLITKV_F32)
     _check(plan._lib, plan._lib.splitkv_attn_backward(plan.handle, ctypes.c_void_p(dev_plan.data_ptr()),
                                                       ctypes.byref(inp), ctypes.byref(gr),
                                                       ctypes.c_void_p(ws.data_ptr()),

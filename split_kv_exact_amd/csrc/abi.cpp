@@ -321,6 +321,8 @@ int splitkv_attn_backward(const splitkv_plan_t* pl, const void* dev_plan, const 
       !aligned16(gr->dv))
     return fail(SPLITKV_ERR_INVALID_ARG, "d_out, out, dq, dk and dv must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(gr->lse) & 3u) != 0) return fail(SPLITKV_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (gr->dkv_dtype != SPLITKV_F32 && gr->dkv_dtype != SPLITKV_BF16)
+    return fail(SPLITKV_ERR_INVALID_ARG, "dkv_dtype must be SPLITKV_F32 or SPLITKV_BF16");
   for (int64_t x : {gr->do_stride_tok, gr->do_stride_head}) {
     if (x < 0 || x % 8 != 0) return fail(SPLITKV_ERR_INVALID_ARG, "d_out strides must be non-negative multiples of 16 bytes");
     if (x > (int64_t(1) << 24)) return fail(SPLITKV_ERR_UNSUPPORTED, "bf16 strides must be at most 2^24 elements");
@@ -366,6 +368,7 @@ int splitkv_attn_backward(const splitkv_plan_t* pl, const void* dev_plan, const 
   b.key_tiles = pl->num_key_tiles;
   b.tiles = reinterpret_cast<const splitkv::KeyTile*>(base + pl->layout.key_tiles);
   b.dq_waves = pl->max_rows <= 128 ? 4 : 8;
+  b.dkv_bf16 = gr->dkv_dtype == SPLITKV_BF16;
   return hip_status(splitkv::launch_backward_bf16(b, pl->D, static_cast<hipStream_t>(hip_stream)),
                     "backward launch");
 }

@@ -28,7 +28,8 @@
 //            per chunk; when g divides 32 a lane's loads are a per-chunk scalar base plus
 //            constant offsets): S = Q K^T, dP = dO V^T, then dV^T += dO^T P and
 //            dK^T += Q^T dS with Q^T and dO^T read by transposing loads. Kept at 168
-//            VGPRs or fewer (three workgroups per CU). dK and dV are written once.
+//            VGPRs or fewer (three workgroups per CU). dK and dV are written once, as
+//            fp32 or rounded to bf16.
 // P and dS enter the matrix cores rounded to bf16 (as P does in the forward); all sums
 // are fp32.
 #include <hip/hip_runtime.h>
@@ -350,7 +351,7 @@ struct KvLds {
   float dd[KV_BUFS][RCH];                           // D_i
 };
 
-template <int D>
+template <int D, bool BF16OUT>
 __global__ __launch_bounds__(256, 3) void dkv_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = BCfg<D>;
@@ -594,12 +595,21 @@ __global__ __launch_bounds__(256, 3) void dkv_kernel(BwdArgs a) {
     buf = buf == KV_BUFS - 1 ? 0 : buf + 1;
   }
   // Store (lane: key li, dims 16 dt + 4 G .. + 3); keys past the sequence are not stored.
+  // bf16 outputs take each fp32 sum rounded to nearest even (8 bytes per lane and tile).
   if (key < n) {
     const int64_t idx = ((sq.kv_base + key) * a.Hkv + kv) * D;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
-      *reinterpret_cast<f32x4*>(a.dk + idx + 16 * dt + 4 * G) = dk[dt] * a.scale;
-      *reinterpret_cast<f32x4*>(a.dv + idx + 16 * dt + 4 * G) = dv[dt];
+      const f32x4 gk = dk[dt] * a.scale, gv = dv[dt];
+      if constexpr (BF16OUT) {
+        const bf16x4 hk = {(__bf16)gk[0], (__bf16)gk[1], (__bf16)gk[2], (__bf16)gk[3]};
+        const bf16x4 hv = {(__bf16)gv[0], (__bf16)gv[1], (__bf16)gv[2], (__bf16)gv[3]};
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.dk) + idx + 16 * dt + 4 * G) = hk;
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.dv) + idx + 16 * dt + 4 * G) = hv;
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.dk) + idx + 16 * dt + 4 * G) = gk;
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.dv) + idx + 16 * dt + 4 * G) = gv;
+      }
     }
   }
 #endif
@@ -624,7 +634,10 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
     if (hipError_t e = hipGetLastError()) return e;
   }
   if (a.key_tiles > 0) {
-    hipLaunchKernelGGL(dkv_kernel<D>, dim3(unsigned(a.key_tiles * a.Hkv)), dim3(256), 0, stream, a);
+    if (a.dkv_bf16)
+      hipLaunchKernelGGL((dkv_kernel<D, true>), dim3(unsigned(a.key_tiles * a.Hkv)), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((dkv_kernel<D, false>), dim3(unsigned(a.key_tiles * a.Hkv)), dim3(256), 0, stream, a);
     if (hipError_t e = hipGetLastError()) return e;
   }
   return hipSuccess;

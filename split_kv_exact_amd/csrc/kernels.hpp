@@ -59,7 +59,7 @@ struct MergeArgs {
   float* lse;
 };
 
-// Arguments of the backward kernels (bf16 inputs, fp32 gradients).
+// Arguments of the backward kernels (bf16 inputs; fp32 dQ, fp32 or bf16 dK and dV).
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -70,8 +70,8 @@ struct BwdArgs {
   const float* out;  // forward O [total_q, Hq, D], contiguous
   const float* lse;  // forward LSE [total_q, Hq]
   float* dq;         // [total_q, Hq, D], contiguous
-  float* dk;         // [total_kv, Hkv, D], contiguous
-  float* dv;
+  void* dk;          // [total_kv, Hkv, D], contiguous, fp32 or bf16 (dkv_bf16)
+  void* dv;
   float* ws_dq;      // per (block, KV head) dQ parts [partial_rows, D]
   float* ws_d;       // D_i = <dO_i, O_i> [total_q * Hq]
   float* ws_l2;      // LSE_i * log2(e) [total_q * Hq], right after ws_d
@@ -90,6 +90,7 @@ struct BwdArgs {
   int64_t key_tiles;  // sum over sequences of ceil(n_s / kDkvTileKeys)
   const KeyTile* tiles;  // where each key tile lies
   int32_t dq_waves;   // waves per dQ workgroup: 4 when every pass has at most 8 row tiles, else 8
+  int32_t dkv_bf16;   // dK and dV stored as bf16 (else fp32)
 };
 
 // Size of the library's own device workspace (splitkv_attn_scratch), one per GPU.

@@ -93,16 +93,18 @@ def backward_flops(wl) -> int:
     return 10 * wl.head_dim * wl.num_q_heads * visible_pairs(wl)
 
 
-def backward_bytes(wl) -> int:
+def backward_bytes(wl, dkv_bytes: int = 4) -> int:
     """Backward pass, each element once: Q, K, V and dO read in the input dtype, O and
-    LSE read and dQ, dK, dV written in fp32."""
+    LSE read and dQ written in fp32, dK and dV written with ``dkv_bytes`` per element
+    (4 for fp32, 2 for bf16)."""
     es = 2 if wl.dtype == "bfloat16" else 4
     d = wl.head_dim
     q_elems = wl.total_q * wl.num_q_heads * d
     kv_elems = wl.total_kv * wl.num_kv_heads * d
     return (2 * q_elems + 2 * kv_elems) * es + (q_elems + wl.total_q * wl.num_q_heads) * 4 \
-        + (q_elems + 2 * kv_elems) * 4
+        + q_elems * 4 + 2 * kv_elems * dkv_bytes
 
 
-def backward_roofline_seconds(wl) -> float:
-    return max(backward_bytes(wl) / (PEAK_HBM_GBS * 1e9), backward_flops(wl) / (PEAK_BF16_MFMA_TFLOPS * 1e12))
+def backward_roofline_seconds(wl, dkv_bytes: int = 4) -> float:
+    return max(backward_bytes(wl, dkv_bytes) / (PEAK_HBM_GBS * 1e9),
+               backward_flops(wl) / (PEAK_BF16_MFMA_TFLOPS * 1e12))

@@ -195,6 +195,10 @@ def test_backward_argument_errors(lib):
              None) == L.SPLITKV_ERR_INVALID_ARG
     assert f(h, dp, ctypes.byref(good), ctypes.byref(grads(do_stride_tok=1 << 25)), ws, nbytes,
              None) == L.SPLITKV_ERR_UNSUPPORTED
+    assert f(h, dp, ctypes.byref(good), ctypes.byref(grads(dkv_dtype=2)), ws, nbytes,
+             None) == L.SPLITKV_ERR_INVALID_ARG
+    assert f(h, dp, ctypes.byref(good), ctypes.byref(grads(dkv_dtype=-1)), ws, nbytes,
+             None) == L.SPLITKV_ERR_INVALID_ARG
     assert f(h, dp, ctypes.byref(good), ctypes.byref(grads()), ws, 16, None) == L.SPLITKV_ERR_WORKSPACE
     lib.splitkv_plan_destroy(h)
 

@@ -74,7 +74,7 @@ def _errors(got, ref):
     return float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-30)), float(np.abs(d).max() / scale)
 
 
-def _forward_backward(wl):
+def _forward_backward(wl, dkv_dtype=torch.float32):
     q, k, v = make_qkv(wl, "cuda")
     do = _do(wl)
     plan = skv.plan_for(wl)
@@ -83,11 +83,27 @@ def _forward_backward(wl):
     ws = skv.workspace(plan)
     ws.fill_(float("nan"))
     dq = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
-    dk = torch.full(k.shape, float("nan"), dtype=torch.float32, device="cuda")
-    dv = torch.full(v.shape, float("nan"), dtype=torch.float32, device="cuda")
+    dk = torch.full(k.shape, float("nan"), dtype=dkv_dtype, device="cuda")
+    dv = torch.full(v.shape, float("nan"), dtype=dkv_dtype, device="cuda")
     skv.splitkv_attn_backward(plan, dev_plan, q, k, v, do, out, lse, ws, dq, dk, dv)
     torch.cuda.synchronize()
     return q, k, v, do, out, lse, dq, dk, dv
+
+
+# dK and dV stored as bf16: each is the fp32 result rounded to nearest even (tested
+# bit for bit against the fp32 call), so the tolerance above still holds with a margin.
+BF16_CASES = [CASES[0], CASES[4], CASES[7], CASES[9], CASES[11]]
+
+
+@pytest.mark.parametrize("wl", BF16_CASES, ids=[w.name for w in BF16_CASES])
+def test_bf16_dkv_is_the_rounded_fp32_result(wl):
+    say(f"[gpu] backward {wl.name}, bf16 dK/dV")
+    a = _forward_backward(wl)
+    b = _forward_backward(wl, torch.bfloat16)
+    assert torch.equal(a[6], b[6]), "dQ does not depend on the dK/dV dtype"
+    for name, x, y in (("dk", a[7], b[7]), ("dv", a[8], b[8])):
+        assert not torch.isnan(y).any(), f"{name} has unwritten entries"
+        assert torch.equal(x.to(torch.bfloat16), y), name
 
 
 @pytest.mark.parametrize("wl", CASES, ids=[w.name for w in CASES])
@@ -125,15 +141,17 @@ def _full_seqs(wl, key):
     return tuple(sorted({0, wl.batch - 1}))
 
 
-@pytest.mark.parametrize("key", ["batch8", "long", "lognormal", "decode", "mixed"])
-def test_full_size_backward_sampled(key):
+@pytest.mark.parametrize("key,dkv", [("batch8", "float32"), ("long", "float32"), ("lognormal", "float32"),
+                                     ("decode", "float32"), ("mixed", "float32"), ("decode", "bfloat16"),
+                                     ("mixed", "bfloat16")])
+def test_full_size_backward_sampled(key, dkv):
     """Full-size workload in the benchmark's launch configuration, checked on sampled
     dQ rows and dK / dV keys of several sequences against the oracle at the GPU's
     forward outputs."""
     torch.cuda.empty_cache()
     wl = get_workload(key)
-    say(f"[gpu] full-size backward {wl.name}")
-    q, k, v, do, out, lse, dq, dk, dv = _forward_backward(wl)
+    say(f"[gpu] full-size backward {wl.name}, {dkv} dK/dV")
+    q, k, v, do, out, lse, dq, dk, dv = _forward_backward(wl, getattr(torch, dkv))
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         assert not torch.isnan(t).any(), f"{name} has unwritten entries"
     rng = np.random.default_rng(5)
