@@ -355,6 +355,7 @@ int splitkv_attn_backward(const splitkv_plan_t* pl, const void* dev_plan, const 
   b.S = pl->S;
   b.jobs = reinterpret_cast<const splitkv::JobRec*>(base + pl->layout.jobs);
   b.num_jobs = int32_t(pl->num_jobs);
+  b.num_fused_jobs = int32_t(pl->num_fused_jobs);
   b.Hq = pl->Hq;
   b.Hkv = pl->Hkv;
   b.g = pl->g;

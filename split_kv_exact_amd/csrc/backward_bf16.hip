@@ -34,6 +34,8 @@
 // are fp32.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "lds_tiles.hpp"
 
@@ -115,6 +117,7 @@ __global__ __launch_bounds__(W * 64, 2) void dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[sizeof(DqLds<D>)];
   DqLds<D>& L = *reinterpret_cast<DqLds<D>*>(smem);
   const JobRec j = a.jobs[blockIdx.x];
+  if (j.flags & kJobFusedKV) return;  // dqkv_small_kernel's job
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int G = lane >> 4, li = lane & 15;
@@ -299,6 +302,329 @@ __global__ __launch_bounds__(W * 64, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt + 4 * G) = acc[t][dt] * a.scale;
     }
+  }
+#endif
+}
+
+// ------------------------------------------------- dQ part, dK and dV of few-row jobs
+// A job flagged kJobFusedKV holds every query row of its KV head (at most kFusedRows,
+// one row tile), so once a stage of keys has been through it, those keys' dK and dV are
+// complete: the block's K/V stream serves dQ and dK/dV alike and the block is read once
+// (the dK/dV kernel's key-tile table leaves these sequences out). Four waves, 32-key
+// stages through the same LDS buffers and swizzles as dq_kernel:
+//   wave 0:     the job's dQ part exactly as dq_kernel forms it (S^T, dP^T, dS^T, then
+//               dQ^T += K^T dS^T), stored at the end;
+//   waves 1, 2: the stage's 16-key tiles 0 and 1: S = Q K^T and dP = dO V^T from the
+//               same register and LDS operands with the operands swapped (lane: key li,
+//               rows 4 G + e), P and dS, then dV^T = dO^T P and dK^T = Q^T dS as
+//               16x16x16 products over the row tile, with Q^T and dO^T held in registers
+//               from the job's start; each key's dK and dV are stored at once;
+//   waves 0, 3: the stage DMA. The storing waves issue none, so no wait on the DMA
+//               counts their stores; they pass the stage barrier without a wait.
+__device__ __forceinline__ void small_wait_barrier(int n) {
+  if (n >= 16)
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  else if (n >= 8)
+    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  else if (n >= 4)
+    asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int D>
+struct SmallLds {
+  DqLds<D> s;                        // the stage buffers, as dq_kernel's
+  unsigned char t[2][16 * D * 4];    // per dK/dV wave: one gradient tile of its 16 keys, row-major
+};
+
+// Store one gradient tile of a dK/dV wave's 16 keys. g[dt] holds this lane's values
+// for key li, dims 16 dt + 4 G .. + 3 (the transposed product's layout, in which a
+// store instruction writes 32- or 16-byte pieces of 16 rows). The tile goes through
+// LDS (16-byte chunks XOR-swizzled by the key's low bits) and leaves as whole rows: a store
+// instruction writes four keys' D contiguous values, 16 bytes per lane. Keys at or
+// past n_keys are not stored; dst is key 0's row.
+template <int D, typename T>
+__device__ __forceinline__ void store_tile_rows(const f32x4 (&g)[D / 16], unsigned char* t, T* dst,
+                                                int64_t key_stride, int n_keys, int lane) {
+  constexpr int RB = D * int(sizeof(T)), NCH = RB / 16;
+  static_assert(NCH % 4 == 0, "whole store instructions");
+  const int G = lane >> 4, li = lane & 15;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const int byte = (16 * dt + 4 * G) * int(sizeof(T));
+    const int off = li * RB + 16 * ((byte / 16) ^ (li & (NCH - 1))) + byte % 16;
+    if constexpr (sizeof(T) == 4) {
+      *reinterpret_cast<f32x4*>(t + off) = g[dt];
+    } else {
+      *reinterpret_cast<bf16x4*>(t + off) = bf16x4{(__bf16)g[dt][0], (__bf16)g[dt][1], (__bf16)g[dt][2], (__bf16)g[dt][3]};
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NCH / 4; ++u) {
+    const int idx = u * 64 + lane, k = idx / NCH, c = idx % NCH;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(t + k * RB + 16 * (c ^ (k & (NCH - 1))));
+    if (k < n_keys) *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(dst + k * key_stride) + 16 * c) = x;
+  }
+}
+
+template <int D, bool BF16OUT>
+__global__ __launch_bounds__(256, 2) void dqkv_small_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using C = BCfg<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[sizeof(SmallLds<D>)];
+  SmallLds<D>& SL = *reinterpret_cast<SmallLds<D>*>(smem);
+  DqLds<D>& L = SL.s;
+  const JobRec j = a.jobs[blockIdx.x];
+  if (!(j.flags & kJobFusedKV)) return;  // dq_kernel's job
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int G = lane >> 4, li = lane & 15;
+  const float c = a.scale * LOG2E;
+
+  // Stage loads by waves 0 and 3 (PW instructions each per tensor), as in dq_kernel.
+  constexpr int NI = DQ_KEYS * C::ROWB / 1024;  // instructions per tile
+  constexpr int PW = NI / 2;
+  static_assert(PW * 2 == NI, "tile split over the two loading waves");
+  const int nst = j.nst * (kStageKeys / DQ_KEYS);
+  // The stage loop every wave runs: one barrier per stage (the loading waves first wait
+  // for their own DMA of the stage), then the next stage's DMA, then body(st, buf).
+  auto stages = [&](bool dma, auto&& body) {
+    const int iw = wave == 0 ? 0 : 1;
+    const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k) + 2 * (j.kv_tok * a.k_st + int64_t(j.kv) * a.k_sh);
+    const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v) + 2 * (j.kv_tok * a.v_st + int64_t(j.kv) * a.v_sh);
+    int srow[PW], kcc[PW], vcc[PW];
+    uint32_t koff[PW], voff[PW];
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      const int p = (iw * PW + u) * 64 + lane;
+      srow[u] = p / C::CH;
+      kcc[u] = swz_tr<C::CH>(srow[u], p % C::CH);
+      vcc[u] = swz_row<C::CH>(srow[u], p % C::CH);
+      koff[u] = uint32_t(srow[u]) * uint32_t(2 * a.k_st) + 16u * kcc[u];
+      voff[u] = uint32_t(srow[u]) * uint32_t(2 * a.v_st) + 16u * vcc[u];
+    }
+    auto issue_stage = [&](int st) {
+      const int buf = st % DQ_BUFS;
+      if ((st + 1) * DQ_KEYS <= j.len) {
+        const unsigned char* ks = kbase + int64_t(st * DQ_KEYS) * (2 * a.k_st);
+        const unsigned char* vs = vbase + int64_t(st * DQ_KEYS) * (2 * a.v_st);
+#pragma unroll
+        for (int u = 0; u < PW; ++u) {
+          const int gi = iw * PW + u;
+          __builtin_amdgcn_global_load_lds(ks + koff[u], (lds_void*)(L.k[buf] + gi * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vs + voff[u], (lds_void*)(L.v[buf] + gi * 1024), 16, 0, 0);
+        }
+        return;
+      }
+#pragma unroll
+      for (int u = 0; u < PW; ++u) {
+        const int key = min(st * DQ_KEYS + srow[u], j.len - 1);  // past the block: its last key (masked)
+        const int gi = iw * PW + u;
+        __builtin_amdgcn_global_load_lds(kbase + int64_t(key) * (2 * a.k_st) + 16 * kcc[u], (lds_void*)(L.k[buf] + gi * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vbase + int64_t(key) * (2 * a.v_st) + 16 * vcc[u], (lds_void*)(L.v[buf] + gi * 1024), 16, 0, 0);
+      }
+    };
+    if (dma)
+      for (int st = 0; st < DQ_BUFS - 1 && st < nst; ++st) issue_stage(st);
+    for (int st = 0; st < nst; ++st) {
+      const int buf = st % DQ_BUFS;
+      if (dma) {
+        small_wait_barrier(2 * PW * min(DQ_BUFS - 2, nst - 1 - st));
+        if (st + DQ_BUFS - 1 < nst) issue_stage(st + DQ_BUFS - 1);  // into the buffer of stage st - 1
+      } else {
+        asm volatile("s_barrier" ::: "memory");
+      }
+      body(st, buf);
+    }
+  };
+  // LDS row-read offsets within a 16-key tile (lane: key li, dims 8 G + 32 dc), K stored
+  // for transposing reads, V for row reads, as in dq_kernel.
+  unsigned ok_row[C::DC], ov_row[C::DC];
+#pragma unroll
+  for (int dc = 0; dc < C::DC; ++dc) {
+    ok_row[dc] = li * C::ROWB + 16 * swz_tr<C::CH>(li, 4 * dc + G);
+    ov_row[dc] = li * C::ROWB + 16 * swz_row<C::CH>(li, 4 * dc + G);
+  }
+  // Row operands (lane: row li, dims 8 G + 32 dc; rows past the last repeat it): the B
+  // operands of S^T = K Q^T and dP^T = V dO^T, and the A operands of S = Q K^T and
+  // dP = dO V^T; and the row's LSE * log2 e, D and last visible block key.
+  const int rq = min(li, j.rows - 1);
+  auto load_rows = [&](bf16x8 (&qop)[C::DC], bf16x8 (&dop)[C::DC], float& lsec, float& dd, int& lim) {
+    const int i = rq / a.g, hl = rq - i * a.g;
+    const int64_t tok = j.q_tok + i, head = int64_t(j.kv) * a.g + hl;
+    const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + tok * a.q_st + head * a.q_sh + 8 * G;
+    const __bf16* gp = reinterpret_cast<const __bf16*>(a.dout) + tok * a.do_st + head * a.do_sh + 8 * G;
+#pragma unroll
+    for (int dc = 0; dc < C::DC; ++dc) {
+      qop[dc] = *reinterpret_cast<const bf16x8*>(qp + 32 * dc);
+      dop[dc] = *reinterpret_cast<const bf16x8*>(gp + 32 * dc);
+    }
+    lsec = a.lse[tok * a.Hq + head] * LOG2E;
+    dd = a.ws_d[tok * a.Hq + head];
+    lim = min(j.lim0 + i, j.len - 1);
+  };
+
+  if (wave == 0) {
+    // The job's dQ part, as dq_kernel forms it for a one-tile job.
+    bf16x8 qop[C::DC], dop[C::DC];
+    float lsec, dd;
+    int lim;
+    load_rows(qop, dop, lsec, dd, lim);
+    unsigned ok_tr[C::DT];
+    {
+      const int e = li >> 2, cc = li & 3, r = 4 * G + e;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) ok_tr[dt] = r * C::ROWB + 16 * swz_tr<C::CH>(r, 2 * dt + (cc >> 1)) + 8 * (cc & 1);
+    }
+    f32x4 acc[C::DT];
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int wave_min_lim = min(j.lim0, j.len - 1);  // row 0's limit, the smallest
+    stages(true, [&](int st, int buf) {
+      const unsigned kb = lds_addr(L.k[buf]), vb = lds_addr(L.v[buf]);
+      const int key0 = st * DQ_KEYS;
+      const bool all_vis = key0 + DQ_KEYS - 1 <= wave_min_lim;
+      float ds[2][4];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        bf16x8 kop[C::DC], vop[C::DC];
+        const unsigned rowoff = unsigned(tt * 16) * C::ROWB;
+#pragma unroll
+        for (int dc = 0; dc < C::DC; ++dc) {
+          kop[dc] = *reinterpret_cast<lds_bf16x8>(uintptr_t(kb + rowoff + ok_row[dc]));
+          vop[dc] = *reinterpret_cast<lds_bf16x8>(uintptr_t(vb + rowoff + ov_row[dc]));
+        }
+        f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < C::DC; ++dc) {
+          x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[dc], qop[dc], x, 0, 0, 0);
+          y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dc], dop[dc], y, 0, 0, 0);
+        }
+        if (all_vis) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ds[tt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c, -lsec)) * (y[e] - dd);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = key0 + 16 * tt + 4 * G + e;
+            const float pr = key <= lim ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c, -lsec)) : 0.f;
+            ds[tt][e] = pr * (y[e] - dd);
+          }
+        }
+      }
+      const bf16x8 dsb = {(__bf16)ds[0][0], (__bf16)ds[0][1], (__bf16)ds[0][2], (__bf16)ds[0][3],
+                          (__bf16)ds[1][0], (__bf16)ds[1][1], (__bf16)ds[1][2], (__bf16)ds[1][3]};
+      unsigned ka[C::DT];
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) ka[dt] = kb + ok_tr[dt];
+      i16x4 lo[C::DT], hi[C::DT];
+      tr_read<0, 16 * C::ROWB>(lo, hi, ka);
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const bf16x8 kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[dt], hi[dt], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, dsb, acc[dt], 0, 0, 0);
+      }
+    });
+    // Store the part (lane: row li, dims 16 dt + 4 G .. + 3), as dq_kernel.
+    float* dst;
+    if (j.flags & kJobSingle) {
+      const int i = rq / a.g, hl = rq - i * a.g;
+      dst = a.dq + ((j.q_tok + i) * a.Hq + int64_t(j.kv) * a.g + hl) * D;
+    } else {
+      dst = a.ws_dq + (j.ws_row + rq) * D;
+    }
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt + 4 * G) = acc[dt] * a.scale;
+  } else if (wave <= 2) {
+    // dK and dV of the stage's 16-key tile tt = wave - 1.
+    const int tt = wave - 1;
+    bf16x8 qop[C::DC], dop[C::DC];
+    float lsec, dd;
+    int lim;
+    load_rows(qop, dop, lsec, dd, lim);
+    // Per row 4 G + e (lane: key li): LSE, D and limit (-1 past the last row, which then
+    // sees no key); Q^T and dO^T as the A operands of the 16x16x16 products (lane: dim
+    // 16 dt + li, rows 4 G .. 4 G + 3; rows past the last read the last row, in bounds,
+    // and are zeroed).
+    float lsek[4], ddk[4];
+    int limk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * G + e;
+      lsek[e] = __shfl(lsec, r);
+      ddk[e] = __shfl(dd, r);
+      limk[e] = r < j.rows ? __shfl(lim, r) : -1;
+    }
+    i16x4 qtr[C::DT], dtr[C::DT];
+    {
+      const short* qs[4];
+      const short* gs[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = min(4 * G + e, j.rows - 1);
+        const int i = r / a.g, hl = r - i * a.g;
+        const int64_t tok = j.q_tok + i, head = int64_t(j.kv) * a.g + hl;
+        qs[e] = reinterpret_cast<const short*>(a.q) + tok * a.q_st + head * a.q_sh + li;
+        gs[e] = reinterpret_cast<const short*>(a.dout) + tok * a.do_st + head * a.do_sh + li;
+      }
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        short qv[4], gv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool in = 4 * G + e < j.rows;
+          qv[e] = in ? qs[e][16 * dt] : short(0);
+          gv[e] = in ? gs[e][16 * dt] : short(0);
+        }
+        qtr[dt] = i16x4{qv[0], qv[1], qv[2], qv[3]};
+        dtr[dt] = i16x4{gv[0], gv[1], gv[2], gv[3]};
+      }
+    }
+    const int64_t kstride = int64_t(a.Hkv) * D;
+    using OutT = typename std::conditional<BF16OUT, __bf16, float>::type;
+    stages(false, [&](int st, int buf) {
+      const unsigned kb = lds_addr(L.k[buf]), vb = lds_addr(L.v[buf]);
+      const unsigned rowoff = unsigned(tt * 16) * C::ROWB;
+      bf16x8 kop[C::DC], vop[C::DC];
+#pragma unroll
+      for (int dc = 0; dc < C::DC; ++dc) {
+        kop[dc] = *reinterpret_cast<lds_bf16x8>(uintptr_t(kb + rowoff + ok_row[dc]));
+        vop[dc] = *reinterpret_cast<lds_bf16x8>(uintptr_t(vb + rowoff + ov_row[dc]));
+      }
+      f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dc = 0; dc < C::DC; ++dc) {
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop[dc], kop[dc], x, 0, 0, 0);
+        y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dop[dc], vop[dc], y, 0, 0, 0);
+      }
+      // Lane: block key kfirst + li, rows 4 G + e.
+      const int kfirst = st * DQ_KEYS + 16 * tt;
+      const int key = kfirst + li;
+      float pr[4], ds[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pr[e] = key <= limk[e] ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], c, -lsek[e])) : 0.f;
+        ds[e] = pr[e] * (y[e] - ddk[e]);
+      }
+      const i16x4 pb = __builtin_bit_cast(i16x4, bf16x4{(__bf16)pr[0], (__bf16)pr[1], (__bf16)pr[2], (__bf16)pr[3]});
+      const i16x4 db = __builtin_bit_cast(i16x4, bf16x4{(__bf16)ds[0], (__bf16)ds[1], (__bf16)ds[2], (__bf16)ds[3]});
+      // dK^T, then dV^T of the 16 keys (lane: key li, dims 16 dt + 4 G + e), each stored
+      // as rows before the next is formed.
+      const int nk = min(16, j.len - kfirst);
+      const int64_t row0 = ((j.kv_tok + kfirst) * a.Hkv + j.kv) * D;
+      f32x4 gr[C::DT];
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+        gr[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qtr[dt], db, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0) * a.scale;
+      store_tile_rows<D, OutT>(gr, SL.t[tt], static_cast<OutT*>(a.dk) + row0, kstride, nk, lane);
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+        gr[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dtr[dt], pb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      store_tile_rows<D, OutT>(gr, SL.t[tt], static_cast<OutT*>(a.dv) + row0, kstride, nk, lane);
+    });
+  } else {
+    stages(true, [](int, int) {});
   }
 #endif
 }
@@ -594,23 +920,22 @@ __global__ __launch_bounds__(256, 3) void dkv_kernel(BwdArgs a) {
     }
     buf = buf == KV_BUFS - 1 ? 0 : buf + 1;
   }
-  // Store (lane: key li, dims 16 dt + 4 G .. + 3); keys past the sequence are not stored.
-  // bf16 outputs take each fp32 sum rounded to nearest even (8 bytes per lane and tile).
-  if (key < n) {
-    const int64_t idx = ((sq.kv_base + key) * a.Hkv + kv) * D;
+  // Store (lane: key li, dims 16 dt + 4 G .. + 3) as whole rows through LDS, each wave
+  // in its own 16 D-float area of the chunk buffers once every wave is past its last
+  // chunk; keys past the sequence are not stored. bf16 outputs take each fp32 sum
+  // rounded to nearest even.
+  static_assert(KV_WAVES * 16 * D * 4 <= int(sizeof(KvLds<D>)), "transpose areas fit the chunk buffers");
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      const f32x4 gk = dk[dt] * a.scale, gv = dv[dt];
-      if constexpr (BF16OUT) {
-        const bf16x4 hk = {(__bf16)gk[0], (__bf16)gk[1], (__bf16)gk[2], (__bf16)gk[3]};
-        const bf16x4 hv = {(__bf16)gv[0], (__bf16)gv[1], (__bf16)gv[2], (__bf16)gv[3]};
-        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.dk) + idx + 16 * dt + 4 * G) = hk;
-        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.dv) + idx + 16 * dt + 4 * G) = hv;
-      } else {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(a.dk) + idx + 16 * dt + 4 * G) = gk;
-        *reinterpret_cast<f32x4*>(static_cast<float*>(a.dv) + idx + 16 * dt + 4 * G) = gv;
-      }
-    }
+  for (int dt = 0; dt < C::DT; ++dt) dk[dt] = dk[dt] * a.scale;
+  {
+    using OutT = typename std::conditional<BF16OUT, __bf16, float>::type;
+    const int64_t kfirst = k0 + 16 * wave;
+    const int nk = int(min<int64_t>(16, n - kfirst));
+    const int64_t row0 = ((sq.kv_base + kfirst) * a.Hkv + kv) * D, kstride = int64_t(a.Hkv) * D;
+    unsigned char* t = smem + wave * (16 * D * 4);
+    store_tile_rows<D, OutT>(dk, t, static_cast<OutT*>(a.dk) + row0, kstride, nk, lane);
+    store_tile_rows<D, OutT>(dv, t, static_cast<OutT*>(a.dv) + row0, kstride, nk, lane);
   }
 #endif
 }
@@ -622,11 +947,19 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(rowdot_kernel<D>, dim3(unsigned((qrows + 3) / 4)), dim3(256), 0, stream, a);
     if (hipError_t e = hipGetLastError()) return e;
   }
-  if (a.num_jobs > 0) {
+  // Both grids cover every job; each kernel returns at once from the other's jobs.
+  if (a.num_jobs > a.num_fused_jobs) {
     if (a.dq_waves == 4)
       hipLaunchKernelGGL((dq_kernel<D, 4>), dim3(unsigned(a.num_jobs)), dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((dq_kernel<D, 8>), dim3(unsigned(a.num_jobs)), dim3(512), 0, stream, a);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  if (a.num_fused_jobs > 0) {
+    if (a.dkv_bf16)
+      hipLaunchKernelGGL((dqkv_small_kernel<D, true>), dim3(unsigned(a.num_jobs)), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((dqkv_small_kernel<D, false>), dim3(unsigned(a.num_jobs)), dim3(256), 0, stream, a);
     if (hipError_t e = hipGetLastError()) return e;
   }
   if (a.total_rows > 0) {

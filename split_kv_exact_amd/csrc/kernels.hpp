@@ -79,6 +79,7 @@ struct BwdArgs {
   int32_t S;
   const JobRec* jobs;
   int32_t num_jobs;
+  int32_t num_fused_jobs;  // of which kJobFusedKV
   int32_t Hq, Hkv, g, causal;
   int64_t total_q;
   // Summing the dQ parts of multi-block sequences (the merge's row mapping).
@@ -87,7 +88,7 @@ struct BwdArgs {
   const MergeGroup* groups;
   int32_t count;
   int64_t total_rows;
-  int64_t key_tiles;  // sum over sequences of ceil(n_s / kDkvTileKeys)
+  int64_t key_tiles;  // entries of the key-tile table (sequences of more than kFusedRows rows)
   const KeyTile* tiles;  // where each key tile lies
   int32_t dq_waves;   // waves per dQ workgroup: 4 when every pass has at most 8 row tiles, else 8
   int32_t dkv_bf16;   // dK and dV stored as bf16 (else fp32)

@@ -262,7 +262,8 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   L.merge_groups_multi = off;
   off = align16(off + sizeof(MergeGroup) * uint64_t(std::max<int64_t>(groups_multi, 1)));
   pl->num_key_tiles = 0;
-  for (int32_t s = 0; s < S; ++s) pl->num_key_tiles += (pl->seqs[s].n + kDkvTileKeys - 1) / kDkvTileKeys;
+  for (int32_t s = 0; s < S; ++s)
+    if (pl->seqs[s].rows > kFusedRows) pl->num_key_tiles += (pl->seqs[s].n + kDkvTileKeys - 1) / kDkvTileKeys;
   L.key_tiles = off;
   off = align16(off + sizeof(KeyTile) * uint64_t(std::max<int64_t>(pl->num_key_tiles, 1)));
 
@@ -304,7 +305,8 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
         const int64_t tmax = std::min<int64_t>(len - 1, int64_t(lim0) + rmax / g);
         j.nst = tmax < 0 ? 1 : int32_t(tmax / kStageKeys) + 1;
         const int32_t wr_log = j.tile_n >= 8 ? 3 : j.tile_n >= 4 ? 2 : j.tile_n >= 2 ? 1 : 0;
-        j.flags = wr_log | (r.rows <= kQTileRows ? kJobQTile : 0) | (r.nb == 1 ? kJobSingle : 0);
+        j.flags = wr_log | (r.rows <= kQTileRows ? kJobQTile : 0) | (r.nb == 1 ? kJobSingle : 0) |
+                  (r.rows <= kFusedRows ? kJobFusedKV : 0);
         jobs.push_back(j);
       }
     }
@@ -454,6 +456,8 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   for (int32_t i = 0; i < nbig; ++i)
     if (jobs[i].tile_n < kPassTiles) pl->mma_partial_passes = true;
   pl->num_jobs = int64_t(jobs.size());
+  pl->num_fused_jobs = 0;
+  for (const JobRec& j : jobs) pl->num_fused_jobs += (j.flags & kJobFusedKV) ? 1 : 0;
   // Queue schedule. The jobs at the end of the LPT order that make up the last fifth
   // of the estimated time form the shared tail, cut into chunks of consecutive jobs of
   // at least min(half the largest job, 1/32 of a worker's average) estimated time.
@@ -606,6 +610,7 @@ void build_plan(const splitkv_problem* p, splitkv_plan_t* pl) {
   fill_groups(reinterpret_cast<MergeGroup*>(base + L.merge_groups_all), ma, nullptr, S, pl->merge_rows_all);
   KeyTile* kt = reinterpret_cast<KeyTile*>(base + L.key_tiles);
   for (int32_t s = 0; s < S; ++s) {
+    if (pl->seqs[s].rows <= kFusedRows) continue;
     const int64_t nt = (pl->seqs[s].n + kDkvTileKeys - 1) / kDkvTileKeys;
     for (int64_t t = 0; t < nt; ++t, ++kt) {
       kt->seq = s;

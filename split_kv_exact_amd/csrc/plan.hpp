@@ -34,9 +34,10 @@ struct splitkv_plan_s {
   int64_t total_q = 0, total_kv = 0, partial_rows = 0;
   int64_t merge_rows_all = 0, merge_rows_multi = 0;
   int32_t num_multi = 0;  // sequences with more than one block
-  int64_t num_key_tiles = 0;  // sum_s ceil(n_s / kDkvTileKeys)
+  int64_t num_key_tiles = 0;  // sum of ceil(n_s / kDkvTileKeys) over sequences of more than kFusedRows rows
   int32_t max_rows = 0;   // max_s q_s * g
   int64_t num_jobs = 0;   // jobs of the bf16 kernels
+  int64_t num_fused_jobs = 0;  // of which flagged kJobFusedKV (backward: dK/dV from the dQ pass)
   int64_t num_mma_jobs = 0;  // of which the matrix-path launch runs the first num_mma_jobs
   bool mma_partial_passes = false;  // some matrix-path job has fewer than kPassTiles row tiles
   int32_t tail_start = 0;  // queue schedule: first job of the shared tail

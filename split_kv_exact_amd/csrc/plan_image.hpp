@@ -55,8 +55,11 @@ static_assert(sizeof(MergeGroup) == 8, "MergeGroup layout");
 constexpr int32_t kMergeCross = int32_t(0x80000000u);
 
 // Keys per workgroup of the backward dK/dV kernel, and each such key tile's place: the
-// sequence and the tile's index within it (tiles numbered sequence by sequence).
+// sequence and the tile's index within it (tiles numbered sequence by sequence). The
+// table lists the tiles of sequences with more than kFusedRows query rows per KV head;
+// the others get their dK and dV in the pass that streams their blocks for dQ.
 constexpr int32_t kDkvTileKeys = 64;
+constexpr int32_t kFusedRows = 16;
 struct KeyTile {
   int32_t seq;
   int32_t tile;
@@ -76,6 +79,8 @@ constexpr int32_t kJobWrMask = 3;   // log2 of the row groups the computing wave
 constexpr int32_t kJobQTile = 4;    // Q rows of the job travel through LDS with stage 0
 constexpr int32_t kJobSingle = 8;   // the sequence has a single block (its result is final)
 constexpr int32_t kJobStream = 16;  // K/V read with the non-temporal hint (the block is not read again later)
+constexpr int32_t kJobFusedKV = 32; // backward: the job holds all of its KV head's query rows (at most
+                                    // kFusedRows), and its block's dK and dV come from the dQ pass
 
 // One job of the bf16 partial-attention kernel: one pass over a block's keys for one
 // KV head and up to kPassTiles row tiles of its query rows. Query row r of a KV head
