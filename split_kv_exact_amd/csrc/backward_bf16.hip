@@ -342,7 +342,8 @@ struct SmallLds {
 // for key li, dims 16 dt + 4 G .. + 3 (the transposed product's layout, in which a
 // store instruction writes 32- or 16-byte pieces of 16 rows). The tile goes through
 // LDS (16-byte chunks XOR-swizzled by the key's low bits) and leaves as whole rows: a store
-// instruction writes four keys' D contiguous values, 16 bytes per lane. Keys at or
+// instruction writes four keys' D contiguous values, 16 bytes per lane, with the
+// non-temporal hint (nothing in the pass reads them again). Keys at or
 // past n_keys are not stored; dst is key 0's row.
 template <int D, typename T>
 __device__ __forceinline__ void store_tile_rows(const f32x4 (&g)[D / 16], unsigned char* t, T* dst,
@@ -364,7 +365,8 @@ __device__ __forceinline__ void store_tile_rows(const f32x4 (&g)[D / 16], unsign
   for (int u = 0; u < NCH / 4; ++u) {
     const int idx = u * 64 + lane, k = idx / NCH, c = idx % NCH;
     const u32x4 x = *reinterpret_cast<const u32x4*>(t + k * RB + 16 * (c ^ (k & (NCH - 1))));
-    if (k < n_keys) *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(dst + k * key_stride) + 16 * c) = x;
+    if (k < n_keys)
+      __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(dst + k * key_stride) + 16 * c));
   }
 }
 

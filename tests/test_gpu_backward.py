@@ -58,6 +58,12 @@ CASES = [
     # table, and dQ sums whose four-row groups straddle sequences.
     _wl("many_short_sequences", [(37 * i) % 400 + 1 for i in range(160)],
         [min((37 * i) % 400 + 1, 1 + i % 4) for i in range(160)], 6, 2, 128, 64, 32),
+    # Sequences at the boundary of the few-row path (at most 16 query rows per KV head:
+    # dK and dV from the dQ pass) and just past it, in one plan: g = 8 with q = 2 (16
+    # rows) and q = 3 (24 rows); a one-key context; ragged 32-key stages; several blocks.
+    _wl("few_row_boundary", [700, 45, 1, 33, 2049, 300], [2, 3, 1, 2, 2, 1], 16, 2, 128, 256, 9),
+    # The few-row path at D = 64 without the causal mask, one- and multi-block.
+    _wl("few_row_d64_noncausal", [300, 64, 513, 17], [1, 4, 2, 3], 8, 2, 64, 128, 5, causal=False),
 ]
 
 
@@ -92,7 +98,7 @@ def _forward_backward(wl, dkv_dtype=torch.float32):
 
 # dK and dV stored as bf16: each is the fp32 result rounded to nearest even (tested
 # bit for bit against the fp32 call), so the tolerance above still holds with a margin.
-BF16_CASES = [CASES[0], CASES[4], CASES[7], CASES[9], CASES[11]]
+BF16_CASES = [CASES[0], CASES[4], CASES[7], CASES[9], CASES[11], CASES[12], CASES[13]]
 
 
 @pytest.mark.parametrize("wl", BF16_CASES, ids=[w.name for w in BF16_CASES])
