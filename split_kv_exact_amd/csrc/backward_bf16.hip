@@ -8,7 +8,7 @@
 //   dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i   (complete within the block),
 //   dQ_i = scale sum_j dS_ij k_j                              (a query-sized part per block,
 //                                                              summed over the blocks).
-// The page describes no kernel; this is a CDNA4 design in four launches:
+// The page describes no kernel; this is a CDNA4 design in up to five launches:
 //   rowdot:  D_i = <dO_i, O_i> for every query row (one wavefront per row);
 //   dq:      one workgroup per forward job (a unit's KV head and up to 256 of its query
 //            rows; 4 waves when no pass has more than 128 rows, so that two workgroups
@@ -19,9 +19,13 @@
 //            transposed as in the forward (S^T = K Q^T), dP^T = V dO^T the same way, and
 //            dQ^T += K^T dS^T with K^T read by transposing LDS loads. The part goes to the
 //            workspace row of (block, KV head), or straight to dQ for one-block sequences;
+//   dqkv_small: the jobs of sequences with at most 16 query rows per KV head (one row
+//            tile holds all of them): the dQ part as dq forms it, and the dK and dV of
+//            each stage's keys from the same K/V stream, so those blocks are read once;
 //   dqsum:   dQ of a multi-block sequence is the sum of its blocks' parts in block order
 //            (one wavefront per row);
-//   dkv:     one workgroup of 4 waves per (sequence, KV head, 64-key tile); a wave holds
+//   dkv:     one workgroup of 4 waves per (sequence, KV head, 64-key tile) of the other
+//            sequences (the plan's key-tile table); a wave holds
 //            its 16 keys' K and V rows in registers and dK^T, dV^T accumulators, and the
 //            query rows that see the tile stream through LDS 32 at a time, with their LSE
 //            and D (direct global->LDS DMA, two chunks ahead, three buffers, one barrier
