@@ -194,3 +194,115 @@ def compare_whole(wl, q, k, v, out, lse, seqs=None, rows_per_task=2048, threads=
     res = Diff(acc["omax"], rel, acc["lmax"])
     res.d2, res.r2 = acc["d2"], acc["r2"]  # sums of squares, to combine parts of one output
     return res
+
+
+class GradDiff:
+    """Whole-tensor errors of dQ, dK and dV: relative L2 and the largest element error
+    relative to the tensor's largest reference magnitude (the backward tolerance's
+    two measures), from sums that combine over parts of one tensor."""
+
+    def __init__(self):
+        self.acc = {t: {"d2": 0.0, "r2": 0.0, "dmax": 0.0, "rmax": 0.0} for t in ("dq", "dk", "dv")}
+
+    def add(self, name, got, ref):
+        a, d = self.acc[name], got - ref
+        a["d2"] += float(np.sum(d * d))
+        a["r2"] += float(np.sum(ref * ref))
+        a["dmax"] = max(a["dmax"], float(np.max(np.abs(d))) if d.size else 0.0)
+        a["rmax"] = max(a["rmax"], float(np.max(np.abs(ref))) if ref.size else 0.0)
+
+    def errors(self, name):
+        a = self.acc[name]
+        return math.sqrt(a["d2"] / max(a["r2"], 1e-300)), a["dmax"] / max(a["rmax"], 1e-30)
+
+    def __str__(self):
+        return ", ".join(f"{t}: rel L2 {self.errors(t)[0]:.2e}, max |d| / max |ref| {self.errors(t)[1]:.2e}"
+                         for t in ("dq", "dk", "dv"))
+
+
+def compare_grads_whole(wl, q, k, v, do, out, lse, dq, dk, dv, seqs=None, keys_per_task=16384, threads=None):
+    """Whole-tensor backward parity: the float64 oracle's gradients at the device's
+    forward outputs (out, lse) for every (sequence, KV head) of the workload (or of
+    ``seqs``), against the device gradients dq [sum q, Hq, D] and dk, dv [sum n, Hkv, D]
+    (any float dtype). One sequence's tensors are copied to the host at a time; each
+    (sequence, KV head) is cut into key ranges that run on a thread pool (BLAS one
+    thread each): a range gives its keys' dK and dV and a part of every row's dQ, and
+    the parts are summed before dQ is compared. Returns a GradDiff."""
+    import threading
+    from concurrent.futures import ThreadPoolExecutor
+
+    import torch
+
+    from oracle.backward import grad_rows
+
+    threads = threads or oracle_threads()
+    g, d = wl.group, wl.head_dim
+    sc = scale_of(wl)
+    qo, ko = offsets(wl.q_lens), offsets(wl.kv_lens)
+    seqs = range(wl.batch) if seqs is None else seqs
+    res = GradDiff()
+    lock = threading.Lock()
+
+    def f64(t):  # exact for bf16, fp32 and fp64 tensors
+        return t.to(torch.float64).numpy()
+
+    def rows_of(t, kap, qs):
+        return t[:, kap * g:(kap + 1) * g].reshape(qs * g, -1) if t.dim() == 3 else t[:, kap * g:(kap + 1) * g].reshape(qs * g)
+
+    def task(s, kap, lo, hi, Q, dO, O, L, pos, kh, vh, gk, gv, dq_part):
+        K, V = f64(kh[lo:hi, kap]), f64(vh[lo:hi, kap])
+        dqp, dkp, dvp = grad_rows(Q, pos - lo, K, V, dO, O, L, sc, wl.causal)
+        gkp, gvp = f64(gk[lo:hi, kap]), f64(gv[lo:hi, kap])
+        assert np.all(np.isfinite(gkp)) and np.all(np.isfinite(gvp)), f"non-finite dK/dV in sequence {s}"
+        with lock:
+            res.add("dk", gkp, dkp)
+            res.add("dv", gvp, dvp)
+            dq_part += dqp
+
+    try:
+        from threadpoolctl import threadpool_limits
+
+        limiter = threadpool_limits(limits=1, user_api="blas")
+    except Exception:
+        limiter = None
+    def finish(s, qs, gq, parts, futs):
+        for f in futs:
+            f.result()
+        for kap, part in enumerate(parts):
+            got = f64(rows_of(gq, kap, qs))
+            assert np.all(np.isfinite(got)), f"non-finite dQ in sequence {s}"
+            res.add("dq", got, part)
+
+    try:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            open_seqs, n_open = [], 0  # sequences whose tasks may still run, oldest first
+            for s in seqs:
+                n, qs = wl.kv_lens[s], wl.q_lens[s]
+                qh, doh = q[qo[s]:qo[s + 1]].detach().cpu(), do[qo[s]:qo[s + 1]].detach().cpu()
+                oh, lh = out[qo[s]:qo[s + 1]].detach().cpu(), lse[qo[s]:qo[s + 1]].detach().cpu()
+                gq = dq[qo[s]:qo[s + 1]].detach().cpu()
+                kh, vh = k[ko[s]:ko[s + 1]].detach().cpu(), v[ko[s]:ko[s + 1]].detach().cpu()
+                gk, gv = dk[ko[s]:ko[s + 1]].detach().cpu(), dv[ko[s]:ko[s + 1]].detach().cpu()
+                pos = np.repeat(np.arange(n - qs, n, dtype=np.int64), g)
+                parts, futs = [], []
+                for kap in range(wl.num_kv_heads):
+                    Q, dO, O = f64(rows_of(qh, kap, qs)), f64(rows_of(doh, kap, qs)), f64(rows_of(oh, kap, qs))
+                    L = f64(rows_of(lh, kap, qs))
+                    part = np.zeros((qs * g, d), dtype=np.float64)
+                    parts.append(part)
+                    for lo in range(0, n, keys_per_task):
+                        futs.append(ex.submit(task, s, kap, lo, min(n, lo + keys_per_task), Q, dO, O, L, pos,
+                                              kh, vh, gk, gv, part))
+                open_seqs.append((s, qs, gq, parts, futs))
+                n_open += len(futs)
+                # Bound the host copies in flight: finish the oldest sequences first.
+                while n_open > 4 * threads and len(open_seqs) > 1:
+                    e = open_seqs.pop(0)
+                    finish(*e)
+                    n_open -= len(e[4])
+            for e in open_seqs:
+                finish(*e)
+    finally:
+        if limiter is not None:
+            limiter.unregister()
+    return res

@@ -5,13 +5,15 @@ The oracle evaluates the textbook gradients at the forward outputs the GPU produ
 cases run the whole oracle; a full-size workload is checked on sampled gradient rows.
 """
 
+import time
+
 import numpy as np
 import pytest
 import torch
 
 import split_kv_exact_amd as skv
 from oracle.backward import attention_grad_ref, grad_sample_ref
-from tests.parity import say
+from tests.parity import compare_grads_whole, say
 from workloads import Workload, get_workload, make_qkv, widen_to_f64
 
 pytestmark = pytest.mark.gpu
@@ -180,5 +182,28 @@ def test_full_size_backward_sampled(key, dkv):
             l2, mx = _errors(got, r)
             say(f"    seq {s} {name}: rel L2 {l2:.2e}, max |d| / max |ref| {mx:.2e}")
             assert l2 <= REL_L2 and mx <= REL_MAX, (s, name, l2, mx)
+    del q, k, v, do, out, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("key,dkv,part", [("batch8", "float32", "all"), ("long", "float32", "all"),
+                                          ("lognormal", "float32", "all"), ("decode", "bfloat16", "all"),
+                                          ("mixed", "float32", "decode"), ("mixed", "bfloat16", "prefill")])
+def test_full_size_backward_whole(key, dkv, part):
+    """Full-size workload in the benchmark's launch configuration, every gradient entry
+    against the float64 oracle at the GPU's forward outputs (the mixed batch in two
+    parts: its 128 decode sequences, then its 4 prefill chunks): relative L2 over each
+    whole tensor and the largest element error against its largest magnitude."""
+    torch.cuda.empty_cache()
+    wl = get_workload(key)
+    seqs = {"all": None, "decode": range(128), "prefill": range(128, 132)}[part]
+    say(f"[gpu] full-size backward {wl.name}, {dkv} dK/dV, whole tensors ({part})")
+    q, k, v, do, out, lse, dq, dk, dv = _forward_backward(wl, getattr(torch, dkv))
+    t0 = time.time()
+    res = compare_grads_whole(wl, q, k, v, do, out, lse, dq, dk, dv, seqs=seqs)
+    say(f"    {time.time() - t0:.0f} s: {res}")
+    for name in ("dq", "dk", "dv"):
+        l2, mx = res.errors(name)
+        assert l2 <= REL_L2 and mx <= REL_MAX, (name, l2, mx)
     del q, k, v, do, out, lse, dq, dk, dv
     torch.cuda.empty_cache()
