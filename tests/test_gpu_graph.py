@@ -66,3 +66,45 @@ def test_graph_replays_match_eager(wl, sched):
         assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"eager step after replay {r}"
     assert int(dev_plan[-1024:].count_nonzero()) == 0, "scheduling area not left zero"
     del graph
+
+
+@pytest.mark.parametrize("dkv", ["float32", "bfloat16"])
+@pytest.mark.parametrize("wl", CASES, ids=[w.name for w in CASES])
+def test_backward_graph_replays_match_eager(wl, dkv):
+    """splitkv_attn_backward captured in a graph (up to five kernel launches, no memset)
+    replays to the eager gradients bit for bit. The ragged case has jobs of all three
+    backward paths (few-row jobs, 8-wave dQ workgroups, dK/dV key tiles)."""
+    say(f"[gpu] backward graph replay {wl.name} {dkv} dK/dV")
+    q, k, v = make_qkv(wl, "cuda")
+    plan = skv.plan_for(wl)
+    dev_plan = skv.splitkv_plan_upload(plan)
+    ws = skv.workspace(plan)
+    out, lse = skv.splitkv_attn(plan, dev_plan, q, k, v, ws)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(99)
+    do = torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32).to(q.dtype)
+    dt = getattr(torch, dkv)
+    dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dk = torch.empty(k.shape, dtype=dt, device="cuda")
+    dv = torch.empty(v.shape, dtype=dt, device="cuda")
+    skv.splitkv_attn_backward(plan, dev_plan, q, k, v, do, out, lse, ws, dq, dk, dv)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (dq, dk, dv)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for _ in range(2):
+                skv.splitkv_attn_backward(plan, dev_plan, q, k, v, do, out, lse, ws, dq, dk, dv, stream=side)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for t in (dq, dk, dv):
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip((dq, dk, dv), ref)), f"replay {r}"
+        skv.splitkv_attn_backward(plan, dev_plan, q, k, v, do, out, lse, ws, dq, dk, dv)
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip((dq, dk, dv), ref)), f"eager call after replay {r}"
+    del graph
