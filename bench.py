@@ -410,7 +410,9 @@ def main() -> int:
                     help="skip the calibration launches that measure the 8 XCDs' relative speeds and re-place "
                          "the plan's workers (most loaded on the fastest XCDs) before timing")
     ap.add_argument("--backward", action="store_true",
-                    help="also time the backward pass (splitkv_attn_backward) and report it under 'backward'")
+                    help="time the backward pass (splitkv_attn_backward) and report it under 'backward' "
+                         "(the default for bf16 workloads; kept for explicit use)")
+    ap.add_argument("--no-backward", action="store_true", help="do not time the backward pass")
     ap.add_argument("--planner-study", action="store_true",
                     help="host only: time the LPT planner against an exact MILP balancer (HiGHS) and write "
                          "the study as JSON, then exit")
@@ -531,7 +533,7 @@ def main() -> int:
         result["sub_runs"] = sub_out
     if flush is not None:
         del flush
-    if args.backward:
+    if not args.no_backward:
         result["backward"] = (_bench_backward(skv, M, wl, q, k, v, stream, args)
                               if wl.dtype == "bfloat16" else None)  # the backward takes bf16 inputs
     if not args.no_cpu_baseline:
@@ -680,8 +682,10 @@ def planner_study(milp_seconds: float = 20.0, full_seconds: float = 60.0, quick:
 
 
 def _bench_backward(skv, M, wl, q, k, v, stream, args):
-    """Times splitkv_attn_backward (its four launches together) at the forward's O and
-    LSE, with a seeded upstream gradient."""
+    """Times splitkv_attn_backward (all its launches together) at the forward's O and
+    LSE, with a seeded upstream gradient, once with fp32 and once with bf16 dK and dV.
+    Mean of back-to-back calls after the same settling as the forward; not part of the
+    headline value."""
     import torch
 
     print("[bench] backward", file=sys.stderr, flush=True)

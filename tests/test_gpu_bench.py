@@ -43,6 +43,11 @@ def test_bench_line_contract(capsys, monkeypatch):
     assert cb["complete"] == (cb["groups_timed"] == cb["groups_total"] == 64) and cb["cpu_model"]
     ex = r["lpt"]["executed"]
     assert ex["static_lists_page_cost"] == round(r["lpt"]["imbalance"], 6)
+    # The backward call is timed by default (bf16 workload), with fp32 and bf16 dK/dV.
+    bw = r["backward"]
+    for key in ("fp32_dkv", "bf16_dkv"):
+        assert bw[key]["ms_per_call"] > 0 and 0 < bw[key]["roofline_fraction"] < 1
+    assert bw["bf16_dkv"]["bytes"] < bw["fp32_dkv"]["bytes"]
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
 
