@@ -207,3 +207,33 @@ def test_full_size_backward_whole(key, dkv, part):
         assert l2 <= REL_L2 and mx <= REL_MAX, (name, l2, mx)
     del q, k, v, do, out, lse, dq, dk, dv
     torch.cuda.empty_cache()
+
+
+def test_caller_scale_forward_and_backward():
+    """A softmax scale other than 1/sqrt(D) (0.3 here, 3.4 times the default for D = 128,
+    so the softmax is much sharper) passed to the forward and the backward call, against
+    the oracle with the same scale; the case has jobs of every forward and backward path."""
+    from oracle import attention_ref
+    from tests.parity import assert_within, compare
+
+    wl, sc = CASES[0], 0.3
+    say(f"[gpu] forward and backward with scale {sc}, {wl.name}")
+    q, k, v = make_qkv(wl, "cuda")
+    do = _do(wl)
+    plan = skv.plan_for(wl)
+    dev_plan = skv.splitkv_plan_upload(plan)
+    out, lse = skv.splitkv_attn(plan, dev_plan, q, k, v, scale=sc)
+    dq, dk, dv = skv.splitkv_attn_backward(plan, dev_plan, q, k, v, do, out, lse, scale=sc)
+    torch.cuda.synchronize()
+    O, L = attention_ref(widen_to_f64(q), widen_to_f64(k), widen_to_f64(v), wl.kv_lens, wl.q_lens,
+                         wl.num_q_heads, wl.num_kv_heads, wl.causal, scale=sc)
+    d = compare(out.cpu().numpy(), O, lse.cpu().numpy(), L)
+    say(f"    forward: {d}")
+    assert_within(d, wl.dtype, "forward with a caller scale")
+    ref = attention_grad_ref(widen_to_f64(q), widen_to_f64(k), widen_to_f64(v), widen_to_f64(do), wl.kv_lens,
+                             wl.q_lens, wl.num_q_heads, wl.num_kv_heads, wl.causal, scale=sc,
+                             o=widen_to_f64(out), lse=widen_to_f64(lse))
+    for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        l2, mx = _errors(widen_to_f64(got), r)
+        say(f"    {name}: rel L2 {l2:.2e}, max |d| / max |ref| {mx:.2e}")
+        assert l2 <= REL_L2 and mx <= REL_MAX, (name, l2, mx)
