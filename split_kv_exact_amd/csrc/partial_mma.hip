@@ -350,19 +350,29 @@ __device__ __forceinline__ void stage(State<D>& st, bf16x8 (&kA)[2][Cfg<D>::DC],
   i16x4 vlo[C::DT], vhi[C::DT];
   bf16x8 kB[2][C::DC];
   // Step A: scores; this step's V^T requested under the softmax, the next step's K
-  // under the P V products.
+  // under the P V products. The matrix-core bursts run at raised wave priority, so that
+  // of the SIMD's two waves the one with products to issue goes first and the other's
+  // softmax fills in behind them (long and mixed 2-3% faster, same GPU).
+  __builtin_amdgcn_s_setprio(1);
   scores<D>(s, st, kA, two);
+  __builtin_amdgcn_s_setprio(0);
   vt_issue<0, 16 * C::ROWB>(vlo, vhi, va);
   softmax<D>(s, st, p, key0, mask, two, c, inv_c);
   vt_wait(vlo, vhi);
   k_read<D, 32 * C::ROWB>(kB, ka);
+  __builtin_amdgcn_s_setprio(1);
   pv<D>(st, p, vlo, vhi, two);
+  __builtin_amdgcn_s_setprio(0);
   // Step B.
+  __builtin_amdgcn_s_setprio(1);
   scores<D>(s, st, kB, two);
+  __builtin_amdgcn_s_setprio(0);
   vt_issue<32 * C::ROWB, 16 * C::ROWB>(vlo, vhi, va);
   softmax<D>(s, st, p, key0 + 32, mask, two, c, inv_c);
   vt_wait(vlo, vhi);
+  __builtin_amdgcn_s_setprio(1);
   pv<D>(st, p, vlo, vhi, two);
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Query row of tile `tile`, lane row li; rows past the last one repeat it.
